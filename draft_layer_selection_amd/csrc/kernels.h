@@ -1,0 +1,150 @@
+// Internal interface between the host driver (knapspec.cpp) and the HIP kernels.
+// Not part of the public ABI: argument structs hold device pointers and sizes only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ks {
+
+enum ActType : int { ACT_F32 = 0, ACT_BF16 = 1 };
+
+// ---------------------------------------------------------------------------------------
+// GEMM: out[r][n] = sum_k A[r][k] * W[n][k] over the rows of one item (all sequences).
+//   mode PARTIAL: fp32 partial sums per K split, P[split][R][ldp]; the consumer adds splits.
+//   mode SWIGLU : split must be 1; 64-column tile t holds gate rows [32t, 32t+32) and up
+//                 rows [ff + 32t, ...); writes H[r][32t + j] = silu(gate) * up.
+// ---------------------------------------------------------------------------------------
+enum GemmMode : int { GEMM_PARTIAL = 0, GEMM_SWIGLU = 1 };
+
+struct GemmArgs {
+  const void* A;  // [R][lda] activations (bf16 or f32, same as W)
+  int lda;
+  int R;          // rows
+  const void* W;  // [N][K] weights
+  int K;
+  int N;          // logical output columns (2*ff for SWIGLU)
+  int n_tiles;    // N / 64
+  int m_tiles;
+  int mb;         // 32-row blocks per tile (bf16 kernel), rows per tile = 32*mb
+  int splits;
+  int k_chunk;    // K per split
+  int mode;
+  float* P;       // PARTIAL output
+  int ldp;
+  void* H;        // SWIGLU output
+  int ldh;
+  int ff;
+  int per_xcd;    // ceil(total tiles / 8): XCD-aware tile order
+};
+
+// ---------------------------------------------------------------------------------------
+// Attention over the shared KV cache (split over context positions) + combine with self.
+// ---------------------------------------------------------------------------------------
+struct AttnSeq {
+  const void* k;  // this layer's K cache of the sequence, [hkv][cap][dh]
+  const void* v;
+  int ctx;        // cached positions
+  int cap;        // positions per head in the buffer
+  int row_off;    // first row of the sequence in this item
+  int M;          // rows of the sequence in this item (live sources + reference)
+  int nsplit;     // context splits
+  int chunk;      // positions per split (multiple of 64)
+};
+
+struct AttnArgs {
+  const void* Q;       // [R][hq][dh] activations (position-rotated, unscaled)
+  int hq, hkv, dh;
+  const int4* work;    // per workgroup: (seq, kv head, q block, split)
+  const AttnSeq* seqs; // [n_seqs]
+  float* Opart;        // [max_split][R*hq][dh] unnormalised partial outputs
+  float* Mpart;        // [max_split][R*hq] running max (log2 domain)
+  float* Lpart;        // [max_split][R*hq] partial denominators
+  int Rtot;
+  float scale_log2;    // log2(e) / sqrt(dh)
+};
+
+struct CombineArgs {
+  const void* Q;
+  const float* kself;  // [R][hkv][dh]
+  const float* vself;
+  const float* Opart;
+  const float* Mpart;
+  const float* Lpart;
+  const AttnSeq* seqs;
+  const int* row_seq;  // [R]
+  int R, hq, hkv, dh;
+  float scale_log2;
+  void* O;             // [R][hq*dh] activations
+};
+
+struct QkvArgs {
+  const float* P;      // [splits][R][ldp]
+  int splits, R, ldp;
+  int hq, hkv, dh;
+  const float* rope;   // [n_seqs][dh] : cos[dh/2] then sin[dh/2]
+  const int* row_seq;  // [R]
+  void* Q;             // [R][hq][dh] activations
+  float* kself;        // [R][hkv][dh]
+  float* vself;
+};
+
+// ---------------------------------------------------------------------------------------
+// Per-budget cosine / execute-or-skip select (+ RMSNorm of the kept state for the next item).
+// ---------------------------------------------------------------------------------------
+struct ItemSeq {   // one (item, sequence)
+  int w;           // item weight
+  int prefix;      // w_0 + ... + w_i
+  int row_off;     // first row of the sequence in this item
+  int M;           // rows (sources + reference)
+  int ref_row;     // global row of the reference in this item's GEMM output
+  int next_ref_row;// global row of the reference in the next item's activations (-1: last)
+  int pad0, pad1;
+};
+
+struct SelectArgs {
+  int item, n_items, B, Bm, d, mw, n_seqs;
+  const float* P;          // [splits][Rtot][d] partial item outputs (before residual)
+  int splits, Rtot;
+  const float* state_old;  // [S][Bm+1][d], index Bm = reference
+  float* state_new;
+  const uint8_t* valid_old;  // [S][Bm]
+  uint8_t* valid_new;
+  const uint64_t* mask_old;  // [S][Bm][mw]
+  uint64_t* mask_new;
+  const int* exec_row;     // [S][Bm] row of this item whose target budget is b, or -1
+  const int* next_row;     // [S][Bm] row of b in the next item's activations, or -1
+  const ItemSeq* info;     // [S]
+  float tau;
+  int skip_cap;
+  float eps;
+  void* xa_next;           // [R_next][d] activations of the next item
+  int act;                 // ActType of xa_next
+  uint8_t* decisions;      // [S][n_items][Bm] or null
+  float* margins;          // [S][n_items][Bm] or null
+  float* cos_out;          // [S][Bm]
+};
+
+struct InitArgs {
+  int n_seqs, Bm, d, mw;
+  const float* const* x0;  // device array [n_seqs] of device pointers
+  float* state;            // [S][Bm+1][d]
+  uint8_t* valid;          // [S][Bm]
+  uint64_t* masks;         // [S][Bm][mw]
+  const int* rows;         // [S][2]: row of budget 0 and of the reference in item 0 (-1 none)
+  void* xa;                // item 0 activations
+  int act;
+  float eps;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
+hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_init(const InitArgs& a, hipStream_t s);
+
+// rows of Q per attention workgroup for the given activation type / head size
+int attention_qblock(int act, int dh);
+
+}  // namespace ks

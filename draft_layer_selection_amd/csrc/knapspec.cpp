@@ -1,0 +1,909 @@
+// Host driver of the KnapSpec DP library: C ABI (include/knapspec.h), argument checking,
+// latency -> integer weights, budget reachability and row maps, the per-item launch sequence
+// on one HIP stream, one synchronisation per solve, and the Tokens-per-Time grid.
+//
+// The method (KnapSpec, arXiv 2602.20217, as described on the pith.science review page):
+// items are the 2L Attention/MLP blocks with latency weights (review, "The reading"), a DP over
+// items x budgets keeps the execute/skip state closer in cosine to the full model (review,
+// "What carries the argument"; referee major comment 1), and a grid over the draft length
+// picks the (set, gamma) pair with the highest Tokens-per-Time (Eq. 4).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "knapspec.h"
+
+#define KS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int PSPLIT_MAX = 8;    // K splits of the partial-output GEMMs
+constexpr int ASPLIT_MAX = 16;   // context splits of the attention
+constexpr int MAX_BUDGETS = 1024;
+constexpr int GAMMA_LIMIT = 64;
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+}  // namespace
+
+struct knapspec_model {
+  knapspec_model_desc desc{};
+  int act = ks::ACT_F32;
+  int elem = 4;
+  int device = 0;
+  std::vector<knapspec_layer_weights> layers;
+  bool have_latency = false;
+  knapspec_latency_model lat{};
+  std::vector<double> per_item;
+
+  // dimensions
+  int L2 = 0, mw = 0, qdim = 0, kvdim = 0, nqkv = 0, Rmax = 0;
+  size_t p_floats = 0;
+
+  // device workspace
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  float* state[2]{};
+  uint8_t* valid[2]{};
+  uint64_t* masks[2]{};
+  void* xa = nullptr;
+  void* q = nullptr;
+  float* kself = nullptr;
+  float* vself = nullptr;
+  void* o = nullptr;
+  void* h = nullptr;
+  float* P = nullptr;
+  float* Opart = nullptr;
+  float* Mpart = nullptr;
+  float* Lpart = nullptr;
+  uint8_t* decisions = nullptr;
+  float* margins = nullptr;
+  float* cos = nullptr;
+  char* maps = nullptr;
+  size_t maps_bytes = 0;
+
+  // profiling (HIP event pairs around each launch)
+  bool profiling = false;
+  std::vector<hipEvent_t> events;
+  std::vector<int> ev_class;
+  int ev_used = 0;
+  double k_ms[KNAPSPEC_KERNEL_CLASSES] = {};
+  int64_t k_count[KNAPSPEC_KERNEL_CLASSES] = {};
+
+  // pinned host staging
+  char* h_maps = nullptr;
+  char* h_out = nullptr;
+  size_t h_out_bytes = 0;
+
+  ~knapspec_model() {
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    if (ws) (void)hipFree(ws);
+    if (h_maps) (void)hipHostFree(h_maps);
+    if (h_out) (void)hipHostFree(h_out);
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// host-only helpers
+// ------------------------------------------------------------------------------------------
+namespace {
+
+int check_latency(const knapspec_latency_model* lat, int n_layers) {
+  if (!lat) return fail(KNAPSPEC_EINVAL, "latency model is NULL");
+  const double v[4] = {lat->attn_base, lat->attn_per_token, lat->mlp, lat->fixed};
+  for (double x : v)
+    if (!std::isfinite(x) || x < 0.0)
+      return fail(KNAPSPEC_EINVAL, "latency values must be finite and >= 0");
+  if (lat->per_item) {
+    for (int i = 0; i < 2 * n_layers; ++i)
+      if (!std::isfinite(lat->per_item[i]) || lat->per_item[i] < 0.0)
+        return fail(KNAPSPEC_EINVAL, "per_item latency %d must be finite and >= 0", i);
+  }
+  return KNAPSPEC_OK;
+}
+
+// Latencies t_i at context n and weights w_i = max(1, rne(t_i / Delta)),
+// Delta = sum(t) / (B - 1) (review, referee major comment 4: w = t / Delta).
+int item_weights(const knapspec_latency_model* lat, int n_layers, int ctx, int B, double* t,
+                 int32_t* w) {
+  const int L2 = 2 * n_layers;
+  std::vector<double> tt(L2);
+  for (int i = 0; i < L2; ++i) {
+    if (lat->per_item)
+      tt[i] = lat->per_item[i];
+    else
+      tt[i] = (i % 2 == 0) ? lat->attn_base + lat->attn_per_token * (double)ctx : lat->mlp;
+  }
+  double total = 0.0;
+  for (int i = 0; i < L2; ++i) total += tt[i];
+  if (!(total > 0.0) || !std::isfinite(total))
+    return fail(KNAPSPEC_EINVAL, "sum of item latencies must be positive and finite");
+  const double delta = total / (double)(B - 1);
+  for (int i = 0; i < L2; ++i) {
+    if (t) t[i] = tt[i];
+    if (w) {
+      const double r = std::nearbyint(tt[i] / delta);  // default rounding: half to even
+      w[i] = (int32_t)std::max(1.0, r);
+    }
+  }
+  return KNAPSPEC_OK;
+}
+
+// Expected accepted tokens 1 + a + ... + a^gamma over the pass time (Eq. 4).
+double tpt_value(double a, int gamma, double t_draft, double t_target) {
+  double num;
+  if (1.0 - a < 1e-6) {
+    double acc = 0.0, p = 1.0;
+    for (int k = 0; k <= gamma; ++k) {
+      acc += p;
+      p *= a;
+    }
+    num = acc;
+  } else {
+    num = (1.0 - std::pow(a, gamma + 1)) / (1.0 - a);
+  }
+  return num / ((double)gamma * t_draft + t_target);
+}
+
+void tpt_grid(const float* alpha, const double* t_draft, const uint8_t* valid, int B,
+              double t_target, int gmin, int gmax, int32_t* bb, int32_t* bg, double* bt) {
+  int best_b = -1, best_g = -1;
+  double best = std::numeric_limits<double>::quiet_NaN();
+  for (int b = 0; b < B; ++b) {
+    if (!valid[b]) continue;
+    double a = (double)alpha[b];
+    if (!(a == a)) a = 0.0;
+    a = std::min(1.0, std::max(0.0, a));
+    for (int g = gmin; g <= gmax; ++g) {
+      const double v = tpt_value(a, g, t_draft[b], t_target);
+      if (best_b < 0 || v > best) {
+        best_b = b;
+        best_g = g;
+        best = v;
+      }
+    }
+  }
+  *bb = best_b;
+  *bg = best_g;
+  *bt = best;
+}
+
+#define HIPCHK(expr)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(KNAPSPEC_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+// ABI
+// ------------------------------------------------------------------------------------------
+KS_API int32_t knapspec_abi_version(void) { return KNAPSPEC_ABI_VERSION; }
+
+KS_API const char* knapspec_last_error(void) { return g_err.c_str(); }
+
+KS_API int32_t knapspec_mask_words(int32_t n_layers) {
+  return n_layers <= 0 ? 0 : (2 * n_layers + 63) / 64;
+}
+
+KS_API int knapspec_item_weights(const knapspec_latency_model* lat, int32_t n_layers,
+                                 int32_t ctx_len, int32_t n_budgets, double* t, int32_t* w) {
+  if (n_layers <= 0) return fail(KNAPSPEC_EINVAL, "n_layers must be > 0");
+  if (ctx_len < 0) return fail(KNAPSPEC_EINVAL, "ctx_len must be >= 0");
+  if (n_budgets < 2) return fail(KNAPSPEC_EINVAL, "n_budgets must be >= 2");
+  int rc = check_latency(lat, n_layers);
+  if (rc) return rc;
+  return item_weights(lat, n_layers, ctx_len, n_budgets, t, w);
+}
+
+KS_API int knapspec_tpt_select(const float* alpha, const double* t_draft, const uint8_t* valid,
+                               int32_t n_budgets, double t_target, int32_t gamma_min,
+                               int32_t gamma_max, int32_t* best_budget, int32_t* best_gamma,
+                               double* best_tpt) {
+  if (!alpha || !t_draft || !valid || !best_budget || !best_gamma || !best_tpt)
+    return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  if (n_budgets < 1) return fail(KNAPSPEC_EINVAL, "n_budgets must be >= 1");
+  if (gamma_min < 1 || gamma_max < gamma_min || gamma_max > GAMMA_LIMIT)
+    return fail(KNAPSPEC_EINVAL, "need 1 <= gamma_min <= gamma_max <= %d", GAMMA_LIMIT);
+  if (!std::isfinite(t_target) || t_target <= 0.0)
+    return fail(KNAPSPEC_EINVAL, "t_target must be finite and > 0");
+  tpt_grid(alpha, t_draft, valid, n_budgets, t_target, gamma_min, gamma_max, best_budget,
+           best_gamma, best_tpt);
+  return KNAPSPEC_OK;
+}
+
+KS_API void knapspec_free_model(knapspec_model* m) { delete m; }
+
+KS_API int knapspec_load_model(const knapspec_model_desc* desc,
+                               const knapspec_layer_weights* layers, void* hip_stream,
+                               knapspec_model** out) {
+  (void)hip_stream;
+  if (!desc || !layers || !out) return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  const knapspec_model_desc& d = *desc;
+  if (d.n_layers <= 0 || d.d_model <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 ||
+      d.head_dim <= 0 || d.d_ff <= 0)
+    return fail(KNAPSPEC_EINVAL, "model dimensions must be positive");
+  if (d.n_q_heads % d.n_kv_heads)
+    return fail(KNAPSPEC_EINVAL, "n_kv_heads must divide n_q_heads");
+  if (d.head_dim % 2) return fail(KNAPSPEC_EINVAL, "head_dim must be even");
+  if (d.dtype != KNAPSPEC_F32 && d.dtype != KNAPSPEC_BF16)
+    return fail(KNAPSPEC_EINVAL, "dtype must be KNAPSPEC_F32 or KNAPSPEC_BF16");
+  if (d.max_budgets < 2 || d.max_budgets > MAX_BUDGETS)
+    return fail(KNAPSPEC_EINVAL, "max_budgets must be in [2, %d]", MAX_BUDGETS);
+  if (d.max_seqs < 1) return fail(KNAPSPEC_EINVAL, "max_seqs must be >= 1");
+  if (d.max_ctx < 0) return fail(KNAPSPEC_EINVAL, "max_ctx must be >= 0");
+  if (!(d.rms_eps > 0.f) || !std::isfinite(d.rms_eps))
+    return fail(KNAPSPEC_EINVAL, "rms_eps must be finite and > 0");
+  if (!(d.rope_theta > 0.f) || !std::isfinite(d.rope_theta))
+    return fail(KNAPSPEC_EINVAL, "rope_theta must be finite and > 0");
+  for (int l = 0; l < d.n_layers; ++l) {
+    const knapspec_layer_weights& w = layers[l];
+    if (!w.w_qkv || !w.w_o || !w.w_gate_up || !w.w_down)
+      return fail(KNAPSPEC_EINVAL, "layer %d has a NULL weight pointer", l);
+  }
+  // shapes the compiled kernels cover
+  if (d.d_model % 4) return fail(KNAPSPEC_EUNSUPPORTED, "d_model must be a multiple of 4");
+  if (d.dtype == KNAPSPEC_BF16) {
+    const int qd = d.n_q_heads * d.head_dim;
+    const int nq = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+    if (d.head_dim != 64 && d.head_dim != 128)
+      return fail(KNAPSPEC_EUNSUPPORTED, "bf16 kernels need head_dim 64 or 128");
+    if (d.d_model % 64 || qd % 64 || nq % 64 || d.d_ff % 64)
+      return fail(KNAPSPEC_EUNSUPPORTED,
+                  "bf16 kernels need d_model, hq*dh, (hq+2hkv)*dh and d_ff multiples of 64");
+  } else {
+    if (d.head_dim != 64 && d.head_dim != 128)
+      return fail(KNAPSPEC_EUNSUPPORTED, "f32 kernels need head_dim 64 or 128");
+    if (d.d_ff % 32) return fail(KNAPSPEC_EUNSUPPORTED, "f32 kernels need d_ff % 32 == 0");
+  }
+
+  // test hook: make the workspace allocation fail so callers' error paths can be exercised
+  const char* fa = std::getenv("KNAPSPEC_TEST_FAIL_ALLOC");
+  if (fa && fa[0] == '1')
+    return fail(KNAPSPEC_ENOMEM, "device workspace allocation failed (forced by test hook)");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0)
+    return fail(KNAPSPEC_EHIP, "no HIP device available");
+
+  knapspec_model* m = new (std::nothrow) knapspec_model();
+  if (!m) return fail(KNAPSPEC_ENOMEM, "host allocation failed");
+  m->desc = d;
+  m->act = d.dtype == KNAPSPEC_BF16 ? ks::ACT_BF16 : ks::ACT_F32;
+  m->elem = d.dtype == KNAPSPEC_BF16 ? 2 : 4;
+  if (hipGetDevice(&m->device) != hipSuccess) {
+    delete m;
+    return fail(KNAPSPEC_EHIP, "hipGetDevice failed");
+  }
+  m->layers.assign(layers, layers + d.n_layers);
+  m->L2 = 2 * d.n_layers;
+  m->mw = knapspec_mask_words(d.n_layers);
+  m->qdim = d.n_q_heads * d.head_dim;
+  m->kvdim = d.n_kv_heads * d.head_dim;
+  m->nqkv = m->qdim + 2 * m->kvdim;
+  const size_t S = d.max_seqs, Bm = d.max_budgets, D = d.d_model;
+  m->Rmax = (int)(S * Bm);
+  const size_t R = m->Rmax;
+  const size_t nmax = std::max<size_t>(m->nqkv, D);
+  m->p_floats = std::max<size_t>(PSPLIT_MAX * std::min<size_t>(R, 256), R) * nmax;
+
+  Carver c;
+  const size_t o_state = c.take(2 * S * (Bm + 1) * D * 4);
+  const size_t o_valid = c.take(2 * S * Bm);
+  const size_t o_masks = c.take(2 * S * Bm * m->mw * 8);
+  const size_t o_xa = c.take(R * D * m->elem);
+  const size_t o_q = c.take(R * m->qdim * m->elem);
+  const size_t o_ks = c.take(R * m->kvdim * 4);
+  const size_t o_vs = c.take(R * m->kvdim * 4);
+  const size_t o_o = c.take(R * m->qdim * m->elem);
+  const size_t o_h = c.take(R * d.d_ff * m->elem);
+  const size_t o_P = c.take(m->p_floats * 4);
+  const size_t o_Op = c.take((size_t)ASPLIT_MAX * R * m->qdim * 4);
+  const size_t o_Mp = c.take((size_t)ASPLIT_MAX * R * d.n_q_heads * 4);
+  const size_t o_Lp = c.take((size_t)ASPLIT_MAX * R * d.n_q_heads * 4);
+  const size_t o_dec = c.take(S * m->L2 * Bm);
+  const size_t o_mar = c.take(S * m->L2 * Bm * 4);
+  const size_t o_cos = c.take(S * Bm * 4);
+  // row maps and launch tables, rebuilt on the host each solve and uploaded once
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const size_t qblocks = (size_t)(G * Bm + 63) / 64;
+  Carver mc;
+  mc.take(2 * (size_t)m->L2 * S * Bm * 4);                                  // exec/next rows
+  mc.take((size_t)m->L2 * R * 4);                                           // row -> seq
+  mc.take((size_t)m->L2 * S * sizeof(ks::ItemSeq));                         // item info
+  mc.take((size_t)d.n_layers * S * d.n_kv_heads * qblocks * ASPLIT_MAX * 16);  // attn work
+  mc.take((size_t)d.n_layers * S * sizeof(ks::AttnSeq));                    // attn seqs
+  mc.take(S * d.head_dim * 4);                                              // rope tables
+  mc.take(S * 8);                                                           // x0 pointers
+  mc.take(S * 2 * 4);                                                       // init rows
+  m->maps_bytes = mc.off;
+  const size_t o_maps = c.take(m->maps_bytes);
+  m->ws_bytes = c.off;
+
+  if (hipMalloc((void**)&m->ws, m->ws_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    const size_t need = m->ws_bytes;
+    m->ws = nullptr;
+    delete m;
+    return fail(KNAPSPEC_ENOMEM, "device workspace allocation of %zu bytes failed", need);
+  }
+  m->h_out_bytes = align_up(S * Bm * m->mw * 8) + align_up(S * Bm * 4) + align_up(S * Bm) +
+                   align_up(S * m->L2 * Bm) + align_up(S * m->L2 * Bm * 4);
+  if (hipHostMalloc((void**)&m->h_maps, m->maps_bytes, hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&m->h_out, m->h_out_bytes, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    delete m;
+    return fail(KNAPSPEC_ENOMEM, "pinned host staging allocation failed");
+  }
+  char* ws = m->ws;
+  m->state[0] = (float*)(ws + o_state);
+  m->state[1] = m->state[0] + S * (Bm + 1) * D;
+  m->valid[0] = (uint8_t*)(ws + o_valid);
+  m->valid[1] = m->valid[0] + S * Bm;
+  m->masks[0] = (uint64_t*)(ws + o_masks);
+  m->masks[1] = m->masks[0] + S * Bm * m->mw;
+  m->xa = ws + o_xa;
+  m->q = ws + o_q;
+  m->kself = (float*)(ws + o_ks);
+  m->vself = (float*)(ws + o_vs);
+  m->o = ws + o_o;
+  m->h = ws + o_h;
+  m->P = (float*)(ws + o_P);
+  m->Opart = (float*)(ws + o_Op);
+  m->Mpart = (float*)(ws + o_Mp);
+  m->Lpart = (float*)(ws + o_Lp);
+  m->decisions = (uint8_t*)(ws + o_dec);
+  m->margins = (float*)(ws + o_mar);
+  m->cos = (float*)(ws + o_cos);
+  m->maps = ws + o_maps;
+  *out = m;
+  return KNAPSPEC_OK;
+}
+
+KS_API int knapspec_set_latency_model(knapspec_model* m, const knapspec_latency_model* lat) {
+  if (!m) return fail(KNAPSPEC_EINVAL, "model is NULL");
+  int rc = check_latency(lat, m->desc.n_layers);
+  if (rc) return rc;
+  m->lat = *lat;
+  if (lat->per_item) {
+    m->per_item.assign(lat->per_item, lat->per_item + m->L2);
+    m->lat.per_item = m->per_item.data();
+  } else {
+    m->per_item.clear();
+    m->lat.per_item = nullptr;
+  }
+  double total = 0.0;
+  if (m->lat.per_item) {
+    for (double v : m->per_item) total += v;
+    if (!(total > 0.0)) return fail(KNAPSPEC_EINVAL, "per_item latencies sum to zero");
+  }
+  m->have_latency = true;
+  return KNAPSPEC_OK;
+}
+
+KS_API int knapspec_set_profiling(knapspec_model* m, int32_t enable) {
+  if (!m) return fail(KNAPSPEC_EINVAL, "model is NULL");
+  m->profiling = enable != 0;
+  for (int c = 0; c < KNAPSPEC_KERNEL_CLASSES; ++c) {
+    m->k_ms[c] = 0.0;
+    m->k_count[c] = 0;
+  }
+  return KNAPSPEC_OK;
+}
+
+KS_API int knapspec_get_kernel_times(const knapspec_model* m, double* total_ms, int64_t* launches,
+                                     int32_t n_classes) {
+  if (!m || !total_ms || !launches) return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  if (n_classes < 0 || n_classes > KNAPSPEC_KERNEL_CLASSES)
+    return fail(KNAPSPEC_EINVAL, "n_classes must be in [0, %d]", KNAPSPEC_KERNEL_CLASSES);
+  for (int c = 0; c < n_classes; ++c) {
+    total_ms[c] = m->k_ms[c];
+    launches[c] = m->k_count[c];
+  }
+  return KNAPSPEC_OK;
+}
+
+namespace {
+
+// Records a start event (class c) when profiling; returns the pair index or -1.
+int prof_begin(knapspec_model* m, int c, hipStream_t st) {
+  if (!m->profiling) return -1;
+  const int k = m->ev_used;
+  if ((size_t)(2 * k + 2) > m->events.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return -1;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return -1;
+    }
+    m->events.push_back(a);
+    m->events.push_back(b);
+    m->ev_class.push_back(c);
+  }
+  m->ev_class[k] = c;
+  if (hipEventRecord(m->events[2 * k], st) != hipSuccess) return -1;
+  m->ev_used = k + 1;
+  return k;
+}
+
+void prof_end(knapspec_model* m, int k, hipStream_t st) {
+  if (k >= 0) (void)hipEventRecord(m->events[2 * k + 1], st);
+}
+
+void prof_collect(knapspec_model* m) {
+  for (int k = 0; k < m->ev_used; ++k) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, m->events[2 * k], m->events[2 * k + 1]) == hipSuccess) {
+      m->k_ms[m->ev_class[k]] += ms;
+      m->k_count[m->ev_class[k]] += 1;
+    }
+  }
+  m->ev_used = 0;
+}
+
+struct SeqPlan {
+  std::vector<double> t;
+  std::vector<int32_t> w;
+  std::vector<int> prefix;
+  // src[i] = sorted source budgets of item i
+  std::vector<std::vector<int>> src;
+};
+
+int choose_splits(int tiles, int K, int kstep, size_t rows, size_t ncols, size_t cap_floats,
+                  int* k_chunk) {
+  const int kiters = (K + kstep - 1) / kstep;
+  int s = 1;
+  while (tiles * s < 512 && s * 2 <= PSPLIT_MAX && kiters / (s * 2) >= 4 &&
+         (size_t)(s * 2) * rows * ncols <= cap_floats)
+    s *= 2;
+  const int per = (kiters + s - 1) / s;
+  *k_chunk = per * kstep;
+  return (kiters + per - 1) / per;
+}
+
+}  // namespace
+
+KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
+                          knapspec_result* res) {
+  if (!m || !args || !res) return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  const knapspec_model_desc& d = m->desc;
+  if (!m->have_latency) return fail(KNAPSPEC_EINVAL, "latency model not set");
+  const int S = args->n_seqs, B = args->n_budgets;
+  if (S < 1 || S > d.max_seqs) return fail(KNAPSPEC_EINVAL, "n_seqs must be in [1, %d]", d.max_seqs);
+  if (!args->seqs) return fail(KNAPSPEC_EINVAL, "seqs is NULL");
+  if (B < 2 || B > d.max_budgets)
+    return fail(KNAPSPEC_EINVAL, "n_budgets must be in [2, %d]", d.max_budgets);
+  if (args->gamma_min < 1 || args->gamma_max < args->gamma_min || args->gamma_max > GAMMA_LIMIT)
+    return fail(KNAPSPEC_EINVAL, "need 1 <= gamma_min <= gamma_max <= %d", GAMMA_LIMIT);
+  if (std::isnan(args->tau)) return fail(KNAPSPEC_EINVAL, "tau is NaN");
+  if (!res->masks || !res->cos || !res->valid || !res->t_draft || !res->item_weight ||
+      !res->best_budget || !res->best_gamma || !res->best_tpt)
+    return fail(KNAPSPEC_EINVAL, "a required result array is NULL");
+  if ((args->flags & KNAPSPEC_RETURN_DECISIONS) && !res->decisions)
+    return fail(KNAPSPEC_EINVAL, "KNAPSPEC_RETURN_DECISIONS set but result.decisions is NULL");
+  if ((args->flags & KNAPSPEC_RETURN_MARGINS) && !res->margins)
+    return fail(KNAPSPEC_EINVAL, "KNAPSPEC_RETURN_MARGINS set but result.margins is NULL");
+  for (int q = 0; q < S; ++q) {
+    const knapspec_seq& sq = args->seqs[q];
+    if (sq.ctx_len < 0 || sq.ctx_len > d.max_ctx)
+      return fail(KNAPSPEC_EINVAL, "seq %d: ctx_len must be in [0, %d]", q, d.max_ctx);
+    if (sq.ctx_capacity < sq.ctx_len)
+      return fail(KNAPSPEC_EINVAL, "seq %d: ctx_capacity < ctx_len", q);
+    if (!sq.x0) return fail(KNAPSPEC_EINVAL, "seq %d: x0 is NULL", q);
+    if (sq.ctx_len > 0) {
+      if (!sq.k_cache || !sq.v_cache) return fail(KNAPSPEC_EINVAL, "seq %d: cache arrays NULL", q);
+      for (int l = 0; l < d.n_layers; ++l)
+        if (!sq.k_cache[l] || !sq.v_cache[l])
+          return fail(KNAPSPEC_EINVAL, "seq %d layer %d: NULL cache pointer", q, l);
+    }
+  }
+  int cur_dev = -1;
+  if (hipGetDevice(&cur_dev) != hipSuccess || cur_dev != m->device)
+    return fail(KNAPSPEC_EINVAL, "current HIP device differs from the model's device");
+
+  const int L2 = m->L2, Bm = d.max_budgets, D = d.d_model, mw = m->mw;
+  const int hq = d.n_q_heads, hkv = d.n_kv_heads, dh = d.head_dim, G = hq / hkv;
+
+  // ---- per-sequence weights and budget reachability (data independent when tau is off;
+  //      the kernels re-check validity on the device, so pruning only removes work).
+  std::vector<SeqPlan> plan(S);
+  for (int q = 0; q < S; ++q) {
+    SeqPlan& p = plan[q];
+    p.t.resize(L2);
+    p.w.resize(L2);
+    int rc = item_weights(&m->lat, d.n_layers, args->seqs[q].ctx_len, B, p.t.data(), p.w.data());
+    if (rc) return rc;
+    p.prefix.resize(L2);
+    p.src.resize(L2);
+    std::vector<uint8_t> reach(B, 0);
+    reach[0] = 1;
+    int pre = 0;
+    for (int i = 0; i < L2; ++i) {
+      const int w = p.w[i];
+      pre += w;
+      p.prefix[i] = pre;
+      for (int s = 0; s + w <= B - 1; ++s)
+        if (reach[s]) p.src[i].push_back(s);
+      for (int s : p.src[i]) reach[s + w] = 1;
+    }
+  }
+  // rows of each item: per sequence [sources..., reference]
+  std::vector<int> Rtot(L2, 0);
+  std::vector<int> row_off((size_t)L2 * S);
+  for (int i = 0; i < L2; ++i) {
+    int r = 0;
+    for (int q = 0; q < S; ++q) {
+      row_off[(size_t)i * S + q] = r;
+      r += (int)plan[q].src[i].size() + 1;
+    }
+    Rtot[i] = r;
+  }
+
+  // ---- build the map/launch tables in pinned host memory
+  Carver mc;
+  const size_t o_exec = mc.take((size_t)L2 * S * Bm * 4);
+  const size_t o_next = mc.take((size_t)L2 * S * Bm * 4);
+  const size_t o_rowseq = mc.take((size_t)L2 * m->Rmax * 4);
+  const size_t o_info = mc.take((size_t)L2 * S * sizeof(ks::ItemSeq));
+  const size_t qb_rows = ks::attention_qblock(m->act, dh);
+  const size_t max_work = (size_t)d.n_layers * S * hkv * ((G * Bm + 63) / 64) * ASPLIT_MAX;
+  const size_t o_work = mc.take(max_work * 16);
+  const size_t o_aseq = mc.take((size_t)d.n_layers * S * sizeof(ks::AttnSeq));
+  const size_t o_rope = mc.take((size_t)S * dh * 4);
+  const size_t o_x0 = mc.take((size_t)S * 8);
+  const size_t o_init = mc.take((size_t)S * 2 * 4);
+  if (mc.off > m->maps_bytes) return fail(KNAPSPEC_EINVAL, "internal: map tables too large");
+  char* hm = m->h_maps;
+  int32_t* exec_row = (int32_t*)(hm + o_exec);
+  int32_t* next_row = (int32_t*)(hm + o_next);
+  int32_t* row_seq = (int32_t*)(hm + o_rowseq);
+  ks::ItemSeq* info = (ks::ItemSeq*)(hm + o_info);
+  int4* work = (int4*)(hm + o_work);
+  ks::AttnSeq* aseq = (ks::AttnSeq*)(hm + o_aseq);
+  float* rope = (float*)(hm + o_rope);
+  const float** x0p = (const float**)(hm + o_x0);
+  int32_t* init_rows = (int32_t*)(hm + o_init);
+
+  std::fill(exec_row, exec_row + (size_t)L2 * S * Bm, -1);
+  std::fill(next_row, next_row + (size_t)L2 * S * Bm, -1);
+  for (int i = 0; i < L2; ++i) {
+    for (int q = 0; q < S; ++q) {
+      const SeqPlan& p = plan[q];
+      const int off = row_off[(size_t)i * S + q];
+      const int M = (int)p.src[i].size() + 1;
+      for (int r = 0; r < M; ++r) row_seq[(size_t)i * m->Rmax + off + r] = q;
+      int32_t* er = exec_row + ((size_t)i * S + q) * Bm;
+      for (int r = 0; r + 1 < M; ++r) er[p.src[i][r] + p.w[i]] = off + r;
+      ks::ItemSeq& in = info[(size_t)i * S + q];
+      in.w = p.w[i];
+      in.prefix = p.prefix[i];
+      in.row_off = off;
+      in.M = M;
+      in.ref_row = off + M - 1;
+      in.next_ref_row = -1;
+      in.pad0 = in.pad1 = 0;
+      if (i + 1 < L2) {
+        const int noff = row_off[(size_t)(i + 1) * S + q];
+        const int nM = (int)p.src[i + 1].size() + 1;
+        int32_t* nr = next_row + ((size_t)i * S + q) * Bm;
+        for (int r = 0; r + 1 < nM; ++r) nr[p.src[i + 1][r]] = noff + r;
+        in.next_ref_row = noff + nM - 1;
+      }
+    }
+  }
+  // attention work lists, one per attention item, in item order
+  std::vector<int> work_off(d.n_layers), work_cnt(d.n_layers);
+  size_t nw = 0;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const int i = 2 * l;
+    int base = 0;
+    for (int q = 0; q < S; ++q)
+      base += hkv * (int)((G * (plan[q].src[i].size() + 1) + qb_rows - 1) / qb_rows);
+    const int target = m->act == ks::ACT_BF16 ? 512 : 1024;
+    work_off[l] = (int)nw;
+    for (int q = 0; q < S; ++q) {
+      const knapspec_seq& sq = args->seqs[q];
+      const int M = (int)plan[q].src[i].size() + 1;
+      const int qblocks = (int)((G * M + qb_rows - 1) / qb_rows);
+      const int ctx = sq.ctx_len;
+      int nsplit = 0, chunk = 64;
+      if (ctx > 0) {
+        int want = std::max(1, (target + base - 1) / base);
+        want = std::min(want, ASPLIT_MAX);
+        want = std::min(want, std::max(1, ctx / 256));
+        chunk = (((ctx + want - 1) / want) + 63) / 64 * 64;
+        nsplit = (ctx + chunk - 1) / chunk;
+      }
+      ks::AttnSeq& as = aseq[(size_t)l * S + q];
+      as.k = ctx > 0 ? sq.k_cache[l] : nullptr;
+      as.v = ctx > 0 ? sq.v_cache[l] : nullptr;
+      as.ctx = ctx;
+      as.cap = sq.ctx_capacity;
+      as.row_off = row_off[(size_t)i * S + q];
+      as.M = M;
+      as.nsplit = nsplit;
+      as.chunk = chunk;
+      for (int c = 0; c < hkv; ++c)
+        for (int qb = 0; qb < qblocks; ++qb)
+          for (int sp = 0; sp < nsplit; ++sp) work[nw++] = make_int4(q, c, qb, sp);
+    }
+    work_cnt[l] = (int)nw - work_off[l];
+  }
+  if (nw > max_work) return fail(KNAPSPEC_EINVAL, "internal: attention work list overflow");
+  // RoPE table at position ctx_len of each sequence: angle_j = n * theta^(-2j/dh) in float64
+  for (int q = 0; q < S; ++q) {
+    const double n = (double)args->seqs[q].ctx_len;
+    for (int j = 0; j < dh / 2; ++j) {
+      const double ang = n * std::pow((double)d.rope_theta, -2.0 * j / (double)dh);
+      rope[(size_t)q * dh + j] = (float)std::cos(ang);
+      rope[(size_t)q * dh + dh / 2 + j] = (float)std::sin(ang);
+    }
+    x0p[q] = args->seqs[q].x0;
+    init_rows[2 * q] = plan[q].src[0].empty() ? -1 : row_off[q];
+    init_rows[2 * q + 1] = row_off[q] + (int)plan[q].src[0].size();
+  }
+
+  hipStream_t st = (hipStream_t)args->hip_stream;
+  char* dm = m->maps;
+  HIPCHK(hipMemcpyAsync(dm, hm, mc.off, hipMemcpyHostToDevice, st));
+  const int32_t* d_exec = (const int32_t*)(dm + o_exec);
+  const int32_t* d_next = (const int32_t*)(dm + o_next);
+  const int32_t* d_rowseq = (const int32_t*)(dm + o_rowseq);
+  const ks::ItemSeq* d_info = (const ks::ItemSeq*)(dm + o_info);
+  const int4* d_work = (const int4*)(dm + o_work);
+  const ks::AttnSeq* d_aseq = (const ks::AttnSeq*)(dm + o_aseq);
+  const float* d_rope = (const float*)(dm + o_rope);
+
+  // ---- DP start
+  int cur = 0;
+  {
+    ks::InitArgs ia{};
+    ia.n_seqs = S;
+    ia.Bm = Bm;
+    ia.d = D;
+    ia.mw = mw;
+    ia.x0 = (const float* const*)(dm + o_x0);
+    ia.state = m->state[0];
+    ia.valid = m->valid[0];
+    ia.masks = m->masks[0];
+    ia.rows = (const int*)(dm + o_init);
+    ia.xa = m->xa;
+    ia.act = m->act;
+    ia.eps = d.rms_eps;
+    const int pk = prof_begin(m, KNAPSPEC_K_INIT, st);
+    HIPCHK(ks::launch_init(ia, st));
+    prof_end(m, pk, st);
+  }
+  const bool want_dec = (args->flags & KNAPSPEC_RETURN_DECISIONS) != 0;
+  const bool want_mar = (args->flags & KNAPSPEC_RETURN_MARGINS) != 0;
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  const int kstep = m->act == ks::ACT_BF16 ? 64 : 32;
+
+  auto gemm = [&](const void* A, int lda, int R, const void* W, int K, int N, int mode,
+                  int* splits_out, int kclass) -> int {
+    ks::GemmArgs g{};
+    g.A = A;
+    g.lda = lda;
+    g.R = R;
+    g.W = W;
+    g.K = K;
+    g.N = N;
+    g.n_tiles = (N + 63) / 64;
+    if (m->act == ks::ACT_BF16) {
+      g.m_tiles = (R + 127) / 128;
+      g.mb = (R + 32 * g.m_tiles - 1) / (32 * g.m_tiles);
+    } else {
+      g.m_tiles = (R + 31) / 32;
+      g.mb = 1;
+    }
+    g.mode = mode;
+    if (mode == ks::GEMM_SWIGLU) {
+      g.splits = 1;
+      g.k_chunk = K;
+      g.H = m->h;
+      g.ldh = d.d_ff;
+      g.ff = d.d_ff;
+      g.n_tiles = (d.d_ff + 31) / 32;
+    } else {
+      g.splits = choose_splits(g.n_tiles * g.m_tiles, K, kstep, R, N, m->p_floats, &g.k_chunk);
+      g.P = m->P;
+      g.ldp = N;
+    }
+    *splits_out = g.splits;
+    const int pk = prof_begin(m, kclass, st);
+    HIPCHK(ks::launch_gemm(g, m->act, st));
+    prof_end(m, pk, st);
+    return KNAPSPEC_OK;
+  };
+
+  for (int i = 0; i < L2; ++i) {
+    const int l = i / 2;
+    const int R = Rtot[i];
+    const knapspec_layer_weights& W = m->layers[l];
+    int splits = 1;
+    int rc;
+    if (i % 2 == 0) {
+      rc = gemm(m->xa, D, R, W.w_qkv, D, m->nqkv, ks::GEMM_PARTIAL, &splits, KNAPSPEC_K_GEMM_QKV);
+      if (rc) return rc;
+      ks::QkvArgs qa{};
+      qa.P = m->P;
+      qa.splits = splits;
+      qa.R = R;
+      qa.ldp = m->nqkv;
+      qa.hq = hq;
+      qa.hkv = hkv;
+      qa.dh = dh;
+      qa.rope = d_rope;
+      qa.row_seq = d_rowseq + (size_t)i * m->Rmax;
+      qa.Q = m->q;
+      qa.kself = m->kself;
+      qa.vself = m->vself;
+      int pk = prof_begin(m, KNAPSPEC_K_QKV_ROPE, st);
+      HIPCHK(ks::launch_qkv(qa, m->act, st));
+      prof_end(m, pk, st);
+      ks::AttnArgs aa{};
+      aa.Q = m->q;
+      aa.hq = hq;
+      aa.hkv = hkv;
+      aa.dh = dh;
+      aa.work = d_work + work_off[l];
+      aa.seqs = d_aseq + (size_t)l * S;
+      aa.Opart = m->Opart;
+      aa.Mpart = m->Mpart;
+      aa.Lpart = m->Lpart;
+      aa.Rtot = R;
+      aa.scale_log2 = scale_log2;
+      pk = prof_begin(m, KNAPSPEC_K_ATTENTION, st);
+      HIPCHK(ks::launch_attention(aa, m->act, work_cnt[l], st));
+      prof_end(m, pk, st);
+      ks::CombineArgs ca{};
+      ca.Q = m->q;
+      ca.kself = m->kself;
+      ca.vself = m->vself;
+      ca.Opart = m->Opart;
+      ca.Mpart = m->Mpart;
+      ca.Lpart = m->Lpart;
+      ca.seqs = d_aseq + (size_t)l * S;
+      ca.row_seq = d_rowseq + (size_t)i * m->Rmax;
+      ca.R = R;
+      ca.hq = hq;
+      ca.hkv = hkv;
+      ca.dh = dh;
+      ca.scale_log2 = scale_log2;
+      ca.O = m->o;
+      pk = prof_begin(m, KNAPSPEC_K_COMBINE, st);
+      HIPCHK(ks::launch_combine(ca, m->act, st));
+      prof_end(m, pk, st);
+      rc = gemm(m->o, m->qdim, R, W.w_o, m->qdim, D, ks::GEMM_PARTIAL, &splits, KNAPSPEC_K_GEMM_O);
+      if (rc) return rc;
+    } else {
+      int s1 = 1;
+      rc = gemm(m->xa, D, R, W.w_gate_up, D, 2 * d.d_ff, ks::GEMM_SWIGLU, &s1,
+                KNAPSPEC_K_GEMM_GATE_UP);
+      if (rc) return rc;
+      rc = gemm(m->h, d.d_ff, R, W.w_down, d.d_ff, D, ks::GEMM_PARTIAL, &splits,
+                KNAPSPEC_K_GEMM_DOWN);
+      if (rc) return rc;
+    }
+    ks::SelectArgs sa{};
+    sa.item = i;
+    sa.n_items = L2;
+    sa.B = B;
+    sa.Bm = Bm;
+    sa.d = D;
+    sa.mw = mw;
+    sa.n_seqs = S;
+    sa.P = m->P;
+    sa.splits = splits;
+    sa.Rtot = R;
+    sa.state_old = m->state[cur];
+    sa.state_new = m->state[cur ^ 1];
+    sa.valid_old = m->valid[cur];
+    sa.valid_new = m->valid[cur ^ 1];
+    sa.mask_old = m->masks[cur];
+    sa.mask_new = m->masks[cur ^ 1];
+    sa.exec_row = d_exec + (size_t)i * S * Bm;
+    sa.next_row = d_next + (size_t)i * S * Bm;
+    sa.info = d_info + (size_t)i * S;
+    sa.tau = args->tau;
+    sa.skip_cap = args->max_skip_weight;
+    sa.eps = d.rms_eps;
+    sa.xa_next = m->xa;
+    sa.act = m->act;
+    sa.decisions = want_dec ? m->decisions : nullptr;
+    sa.margins = want_mar ? m->margins : nullptr;
+    sa.cos_out = m->cos;
+    const int pks = prof_begin(m, KNAPSPEC_K_SELECT, st);
+    HIPCHK(ks::launch_select(sa, st));
+    prof_end(m, pks, st);
+    cur ^= 1;
+  }
+
+  // ---- results back to the host (one synchronisation)
+  char* ho = m->h_out;
+  Carver oc;
+  const size_t ho_masks = oc.take((size_t)S * Bm * mw * 8);
+  const size_t ho_cos = oc.take((size_t)S * Bm * 4);
+  const size_t ho_valid = oc.take((size_t)S * Bm);
+  const size_t ho_dec = oc.take((size_t)S * L2 * Bm);
+  const size_t ho_mar = oc.take((size_t)S * L2 * Bm * 4);
+  HIPCHK(hipMemcpyAsync(ho + ho_masks, m->masks[cur], (size_t)S * Bm * mw * 8,
+                        hipMemcpyDeviceToHost, st));
+  HIPCHK(hipMemcpyAsync(ho + ho_cos, m->cos, (size_t)S * Bm * 4, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipMemcpyAsync(ho + ho_valid, m->valid[cur], (size_t)S * Bm, hipMemcpyDeviceToHost, st));
+  if (want_dec)
+    HIPCHK(hipMemcpyAsync(ho + ho_dec, m->decisions, (size_t)S * L2 * Bm, hipMemcpyDeviceToHost, st));
+  if (want_mar)
+    HIPCHK(hipMemcpyAsync(ho + ho_mar, m->margins, (size_t)S * L2 * Bm * 4, hipMemcpyDeviceToHost,
+                          st));
+  HIPCHK(hipStreamSynchronize(st));
+  if (m->profiling) prof_collect(m);
+
+  const uint64_t* hmask = (const uint64_t*)(ho + ho_masks);
+  const float* hcos = (const float*)(ho + ho_cos);
+  const uint8_t* hvalid = (const uint8_t*)(ho + ho_valid);
+  const double fixed = m->lat.fixed;
+  for (int q = 0; q < S; ++q) {
+    const SeqPlan& p = plan[q];
+    for (int b = 0; b < B; ++b) {
+      const size_t src = (size_t)q * Bm + b, dst = (size_t)q * B + b;
+      std::memcpy(res->masks + dst * mw, hmask + src * mw, (size_t)mw * 8);
+      res->cos[dst] = hvalid[src] ? hcos[src] : std::numeric_limits<float>::quiet_NaN();
+      res->valid[dst] = hvalid[src];
+      double td = fixed;
+      for (int i = 0; i < L2; ++i)
+        if ((hmask[src * mw + i / 64] >> (i % 64)) & 1ull) td += p.t[i];
+      res->t_draft[dst] = td;
+    }
+    for (int i = 0; i < L2; ++i) res->item_weight[(size_t)q * L2 + i] = p.w[i];
+    double t_target = fixed;
+    for (int i = 0; i < L2; ++i) t_target += p.t[i];
+    if (!(t_target > 0.0)) return fail(KNAPSPEC_EINVAL, "target pass latency must be > 0");
+    tpt_grid(res->cos + (size_t)q * B, res->t_draft + (size_t)q * B, res->valid + (size_t)q * B, B,
+             t_target, args->gamma_min, args->gamma_max, res->best_budget + q,
+             res->best_gamma + q, res->best_tpt + q);
+    if (want_dec) {
+      const uint8_t* hd = (const uint8_t*)(ho + ho_dec);
+      for (int i = 0; i < L2; ++i)
+        std::memcpy(res->decisions + ((size_t)q * L2 + i) * B, hd + ((size_t)q * L2 + i) * Bm, B);
+    }
+    if (want_mar) {
+      const float* hmr = (const float*)(ho + ho_mar);
+      for (int i = 0; i < L2; ++i)
+        std::memcpy(res->margins + ((size_t)q * L2 + i) * B, hmr + ((size_t)q * L2 + i) * Bm,
+                    (size_t)B * 4);
+    }
+  }
+  return KNAPSPEC_OK;
+}

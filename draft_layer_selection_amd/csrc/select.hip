@@ -1,0 +1,227 @@
+// Per-budget execute/skip select of the KnapSpec DP and the DP's initial state.
+//
+// One workgroup per (sequence, budget b) and one per sequence for the full-model reference.
+// The item's GEMM wrote fp32 K-split partials of F_i(x) - x for each source row; this kernel
+// adds the splits and the residual in a fixed order, forms
+//   c_exec = cos(g[b - w_i] + dF, ref'),   c_skip = cos(g[b], ref'),   ref' = ref + dF_ref,
+// keeps the larger (skip on exact ties, NaN as -inf), applies the tau / skip-cap pruning,
+// carries the layer mask, and writes the kept state together with its RMSNorm'd copy in the
+// activation layout of the next item's GEMM (so the norm is fused into the select).
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ks {
+
+namespace {
+
+constexpr int SEL_THREADS = 256;
+
+// value of element e of a GEMM row after adding its K splits (fixed order) and the residual
+__device__ __forceinline__ f32x4 row_value(const float* P, int splits, size_t split_stride,
+                                           size_t row_off, const float* res, int e4) {
+  f32x4 v = *(const f32x4*)(P + row_off + 4 * e4);
+  for (int s = 1; s < splits; ++s) {
+    const f32x4 p = *(const f32x4*)(P + s * split_stride + row_off + 4 * e4);
+    v += p;
+  }
+  const f32x4 r = *(const f32x4*)(res + 4 * e4);
+  return r + v;
+}
+
+template <int N>
+__device__ __forceinline__ void block_sum(float (&v)[N], float* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = warp_sum(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) scratch[wave * N + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float t = scratch[i];
+    for (int w = 1; w < SEL_THREADS / 64; ++w) t += scratch[w * N + i];
+    v[i] = t;
+  }
+  __syncthreads();
+}
+
+template <class T>
+__device__ __forceinline__ void store_act(void* xa, size_t row, int d, int e4, f32x4 x,
+                                          float scale) {
+  T* p = (T*)xa + row * d + 4 * e4;
+  p[0] = from_f32<T>(x[0] * scale);
+  p[1] = from_f32<T>(x[1] * scale);
+  p[2] = from_f32<T>(x[2] * scale);
+  p[3] = from_f32<T>(x[3] * scale);
+}
+
+__device__ __forceinline__ float nan_to_ninf(float c) { return (c == c) ? c : -INFINITY; }
+
+template <class T>
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
+  const int q = blockIdx.x / (a.B + 1);
+  const int b = blockIdx.x % (a.B + 1);
+  const bool is_ref = b == a.B;
+  const ItemSeq inf = a.info[q];
+  const int d4 = a.d / 4;
+  const size_t sstride = (size_t)(a.Bm + 1) * a.d;  // per-sequence state stride
+  const float* st_old = a.state_old + q * sstride;
+  float* st_new = a.state_new + q * sstride;
+  const size_t split_stride = (size_t)a.Rtot * a.d;
+  const size_t ref_poff = (size_t)inf.ref_row * a.d;
+  const float* ref_res = st_old + (size_t)a.Bm * a.d;
+  __shared__ float scratch[8 * (SEL_THREADS / 64)];
+
+  if (is_ref) {
+    float ss[1] = {0.f};
+    for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+      const f32x4 r = row_value(a.P, a.splits, split_stride, ref_poff, ref_res, e4);
+      *(f32x4*)(st_new + (size_t)a.Bm * a.d + 4 * e4) = r;
+      ss[0] += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
+    }
+    if (inf.next_ref_row < 0) return;
+    block_sum<1>(ss, scratch);
+    const float scale = 1.0f / sqrtf(ss[0] / (float)a.d + a.eps);
+    for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+      const f32x4 r = *(const f32x4*)(st_new + (size_t)a.Bm * a.d + 4 * e4);
+      store_act<T>(a.xa_next, inf.next_ref_row, a.d, e4, r, scale);
+    }
+    return;
+  }
+
+  const int qb = q * a.Bm + b;
+  const int erow = a.exec_row[qb];
+  const int src = b - inf.w;
+  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
+  const bool has_skip = a.valid_old[qb] != 0;
+  const size_t epoff = has_exec ? (size_t)erow * a.d : 0;
+  const float* e_res = st_old + (size_t)(has_exec ? src : 0) * a.d;
+  const float* g_row = st_old + (size_t)b * a.d;
+
+  // pass 1: rr, er, ee, gr, gg
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  if (has_exec || has_skip) {
+    for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+      const f32x4 r = row_value(a.P, a.splits, split_stride, ref_poff, ref_res, e4);
+      acc[0] += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
+      if (has_exec) {
+        const f32x4 ev = row_value(a.P, a.splits, split_stride, epoff, e_res, e4);
+        acc[1] += ev[0] * r[0] + ev[1] * r[1] + ev[2] * r[2] + ev[3] * r[3];
+        acc[2] += ev[0] * ev[0] + ev[1] * ev[1] + ev[2] * ev[2] + ev[3] * ev[3];
+      }
+      if (has_skip) {
+        const f32x4 gv = *(const f32x4*)(g_row + 4 * e4);
+        acc[3] += gv[0] * r[0] + gv[1] * r[1] + gv[2] * r[2] + gv[3] * r[3];
+        acc[4] += gv[0] * gv[0] + gv[1] * gv[1] + gv[2] * gv[2] + gv[3] * gv[3];
+      }
+    }
+  }
+  block_sum<5>(acc, scratch);
+  const float c_e = has_exec ? nan_to_ninf(acc[1] / (sqrtf(acc[2]) * sqrtf(acc[0]))) : -INFINITY;
+  const float c_s = has_skip ? nan_to_ninf(acc[3] / (sqrtf(acc[4]) * sqrtf(acc[0]))) : -INFINITY;
+  const bool take = c_e > c_s;
+  const float best = take ? c_e : c_s;
+  bool alive = best > -INFINITY;
+  if (best < a.tau) alive = false;
+  if (a.skip_cap >= 0 && inf.prefix - b > a.skip_cap) alive = false;
+
+  if (threadIdx.x == 0) {
+    a.valid_new[qb] = alive ? 1 : 0;
+    const size_t cell = ((size_t)q * a.n_items + a.item) * a.Bm + b;
+    if (a.decisions) a.decisions[cell] = alive ? (take ? 1 : 0) : 255;
+    if (a.margins) {
+      const bool he = c_e > -INFINITY, hs = c_s > -INFINITY;
+      a.margins[cell] = (he && hs) ? fabsf(c_e - c_s) : ((he != hs) ? INFINITY : NAN);
+    }
+    if (a.item == a.n_items - 1) a.cos_out[qb] = alive ? best : NAN;
+  }
+  if (threadIdx.x < a.mw) {
+    const int wd = threadIdx.x;
+    uint64_t mval = 0;
+    if (alive) {
+      if (take) {
+        mval = a.mask_old[((size_t)q * a.Bm + src) * a.mw + wd];
+        if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
+      } else {
+        mval = a.mask_old[(size_t)qb * a.mw + wd];
+      }
+    }
+    a.mask_new[(size_t)qb * a.mw + wd] = mval;
+  }
+
+  // pass 2: kept state and its RMSNorm'd activation row for the next item
+  const int nrow = a.next_row[qb];
+  if (!alive) {
+    if (nrow >= 0) {
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        store_act<T>(a.xa_next, nrow, a.d, e4, z, 0.f);
+      }
+    }
+    return;
+  }
+  const float ms = (take ? acc[2] : acc[4]) / (float)a.d;
+  const float scale = 1.0f / sqrtf(ms + a.eps);
+  float* out = st_new + (size_t)b * a.d;
+  for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+    const f32x4 x = take ? row_value(a.P, a.splits, split_stride, epoff, e_res, e4)
+                         : *(const f32x4*)(g_row + 4 * e4);
+    *(f32x4*)(out + 4 * e4) = x;
+    if (nrow >= 0) store_act<T>(a.xa_next, nrow, a.d, e4, x, scale);
+  }
+}
+
+// DP start: budget 0 and the reference hold x0; every other budget is empty.
+template <class T>
+__global__ __launch_bounds__(SEL_THREADS) void init_kernel(InitArgs a) {
+  const int q = blockIdx.x;
+  const float* x0 = a.x0[q];
+  const size_t sstride = (size_t)(a.Bm + 1) * a.d;
+  float* st = a.state + q * sstride;
+  for (int b = threadIdx.x; b < a.Bm; b += SEL_THREADS) a.valid[q * a.Bm + b] = b == 0 ? 1 : 0;
+  for (int i = threadIdx.x; i < a.Bm * a.mw; i += SEL_THREADS)
+    a.masks[(size_t)q * a.Bm * a.mw + i] = 0;
+  __shared__ float scratch[SEL_THREADS / 64];
+  const int d4 = a.d / 4;
+  float ss[1] = {0.f};
+  for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+    const f32x4 x = *(const f32x4*)(x0 + 4 * e4);
+    *(f32x4*)(st + 4 * e4) = x;
+    *(f32x4*)(st + (size_t)a.Bm * a.d + 4 * e4) = x;
+    ss[0] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  }
+  block_sum<1>(ss, scratch);
+  const float scale = 1.0f / sqrtf(ss[0] / (float)a.d + a.eps);
+  const int r0 = a.rows[2 * q], rref = a.rows[2 * q + 1];
+  for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+    const f32x4 x = *(const f32x4*)(x0 + 4 * e4);
+    if (r0 >= 0) store_act<T>(a.xa, r0, a.d, e4, x, scale);
+    if (rref >= 0) store_act<T>(a.xa, rref, a.d, e4, x, scale);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_seqs * (a.B + 1)), block(SEL_THREADS);
+  if (a.act == ACT_F32)
+    hipLaunchKernelGGL(select_kernel<float>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(select_kernel<bf16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_init(const InitArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_seqs), block(SEL_THREADS);
+  if (a.act == ACT_F32)
+    hipLaunchKernelGGL(init_kernel<float>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(init_kernel<bf16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ks

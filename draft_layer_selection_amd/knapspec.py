@@ -1,0 +1,258 @@
+"""ctypes binding of libknapspec.so (the C ABI in include/knapspec.h).
+
+Argument marshalling only: every step of the DP runs in the library's HIP kernels.  The
+functions keep the C names; ``Model`` is a convenience wrapper that fills the C structs from
+torch tensors (device memory and streams come from PyTorch, nothing else does).
+If the shared library is missing this module raises on import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("KNAPSPEC_LIB", os.path.join(_HERE, "libknapspec.so"))
+
+KNAPSPEC_OK = 0
+KNAPSPEC_EINVAL = -1
+KNAPSPEC_ENOMEM = -2
+KNAPSPEC_EHIP = -3
+KNAPSPEC_EUNSUPPORTED = -4
+KNAPSPEC_F32 = 0
+KNAPSPEC_BF16 = 1
+KNAPSPEC_RETURN_DECISIONS = 1
+KNAPSPEC_RETURN_MARGINS = 2
+KERNEL_CLASSES = ["init", "gemm_qkv", "qkv_rope", "attention", "combine", "gemm_o",
+                  "gemm_gate_up", "gemm_down", "select"]
+
+
+class knapspec_model_desc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ff", C.c_int32),
+                ("dtype", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                ("max_budgets", C.c_int32), ("max_seqs", C.c_int32), ("max_ctx", C.c_int32)]
+
+
+class knapspec_layer_weights(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_o", C.c_void_p), ("w_gate_up", C.c_void_p),
+                ("w_down", C.c_void_p)]
+
+
+class knapspec_latency_model(C.Structure):
+    _fields_ = [("attn_base", C.c_double), ("attn_per_token", C.c_double), ("mlp", C.c_double),
+                ("fixed", C.c_double), ("per_item", C.POINTER(C.c_double))]
+
+
+class knapspec_seq(C.Structure):
+    _fields_ = [("ctx_len", C.c_int32), ("ctx_capacity", C.c_int32),
+                ("k_cache", C.POINTER(C.c_void_p)), ("v_cache", C.POINTER(C.c_void_p)),
+                ("x0", C.c_void_p)]
+
+
+class knapspec_solve_args(C.Structure):
+    _fields_ = [("n_seqs", C.c_int32), ("seqs", C.POINTER(knapspec_seq)),
+                ("n_budgets", C.c_int32), ("gamma_min", C.c_int32), ("gamma_max", C.c_int32),
+                ("tau", C.c_float), ("max_skip_weight", C.c_int32), ("flags", C.c_int32),
+                ("hip_stream", C.c_void_p)]
+
+
+class knapspec_result(C.Structure):
+    _fields_ = [("masks", C.POINTER(C.c_uint64)), ("cos", C.POINTER(C.c_float)),
+                ("valid", C.POINTER(C.c_uint8)), ("t_draft", C.POINTER(C.c_double)),
+                ("item_weight", C.POINTER(C.c_int32)), ("best_budget", C.POINTER(C.c_int32)),
+                ("best_gamma", C.POINTER(C.c_int32)), ("best_tpt", C.POINTER(C.c_double)),
+                ("decisions", C.POINTER(C.c_uint8)), ("margins", C.POINTER(C.c_float))]
+
+
+# symbol -> (restype, argtypes); every entry point of include/knapspec.h
+SIGNATURES = {
+    "knapspec_load_model": (C.c_int, [C.POINTER(knapspec_model_desc),
+                                      C.POINTER(knapspec_layer_weights), C.c_void_p,
+                                      C.POINTER(C.c_void_p)]),
+    "knapspec_set_latency_model": (C.c_int, [C.c_void_p, C.POINTER(knapspec_latency_model)]),
+    "knapspec_solve": (C.c_int, [C.c_void_p, C.POINTER(knapspec_solve_args),
+                                 C.POINTER(knapspec_result)]),
+    "knapspec_tpt_select": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_double),
+                                      C.POINTER(C.c_uint8), C.c_int32, C.c_double, C.c_int32,
+                                      C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                      C.POINTER(C.c_double)]),
+    "knapspec_item_weights": (C.c_int, [C.POINTER(knapspec_latency_model), C.c_int32, C.c_int32,
+                                        C.c_int32, C.POINTER(C.c_double),
+                                        C.POINTER(C.c_int32)]),
+    "knapspec_set_profiling": (C.c_int, [C.c_void_p, C.c_int32]),
+    "knapspec_get_kernel_times": (C.c_int, [C.c_void_p, C.POINTER(C.c_double),
+                                            C.POINTER(C.c_int64), C.c_int32]),
+    "knapspec_mask_words": (C.c_int32, [C.c_int32]),
+    "knapspec_free_model": (None, [C.c_void_p]),
+    "knapspec_last_error": (C.c_char_p, []),
+    "knapspec_abi_version": (C.c_int32, []),
+}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first "
+                      "(there is no CPU fallback)")
+lib = C.CDLL(LIB_PATH)
+for _name, (_res, _args) in SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+knapspec_load_model = lib.knapspec_load_model
+knapspec_set_latency_model = lib.knapspec_set_latency_model
+knapspec_solve = lib.knapspec_solve
+knapspec_tpt_select = lib.knapspec_tpt_select
+knapspec_item_weights = lib.knapspec_item_weights
+knapspec_set_profiling = lib.knapspec_set_profiling
+knapspec_get_kernel_times = lib.knapspec_get_kernel_times
+knapspec_mask_words = lib.knapspec_mask_words
+knapspec_free_model = lib.knapspec_free_model
+knapspec_last_error = lib.knapspec_last_error
+knapspec_abi_version = lib.knapspec_abi_version
+
+
+class KnapSpecError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = knapspec_last_error().decode(errors="replace")
+        super().__init__(f"{where} failed with {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int, where: str):
+    if rc != KNAPSPEC_OK:
+        raise KnapSpecError(rc, where)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+def latency_struct(attn_base, attn_per_token, mlp, fixed=0.0, per_item=None):
+    lat = knapspec_latency_model(attn_base, attn_per_token, mlp, fixed, None)
+    keep = None
+    if per_item is not None:
+        keep = np.ascontiguousarray(per_item, dtype=np.float64)
+        lat.per_item = _ptr(keep, C.c_double)
+    return lat, keep
+
+
+def tpt_select(alpha, t_draft, valid, t_target, gamma_min, gamma_max):
+    """knapspec_tpt_select on numpy arrays -> (best_budget, best_gamma, best_tpt)."""
+    a = np.ascontiguousarray(alpha, dtype=np.float32)
+    t = np.ascontiguousarray(t_draft, dtype=np.float64)
+    v = np.ascontiguousarray(valid, dtype=np.uint8)
+    bb, bg, bt = C.c_int32(), C.c_int32(), C.c_double()
+    _check(knapspec_tpt_select(_ptr(a, C.c_float), _ptr(t, C.c_double), _ptr(v, C.c_uint8),
+                               len(a), float(t_target), int(gamma_min), int(gamma_max),
+                               C.byref(bb), C.byref(bg), C.byref(bt)), "knapspec_tpt_select")
+    return bb.value, bg.value, bt.value
+
+
+def item_weights(n_layers, ctx, n_budgets, attn_base, attn_per_token, mlp, fixed=0.0,
+                 per_item=None):
+    lat, keep = latency_struct(attn_base, attn_per_token, mlp, fixed, per_item)
+    t = np.zeros(2 * n_layers, dtype=np.float64)
+    w = np.zeros(2 * n_layers, dtype=np.int32)
+    _check(knapspec_item_weights(C.byref(lat), n_layers, ctx, n_budgets, _ptr(t, C.c_double),
+                                 _ptr(w, C.c_int32)), "knapspec_item_weights")
+    return t, w
+
+
+class Result:
+    """Host arrays of one solve (numpy views of what the library filled)."""
+
+    def __init__(self, n_seqs, n_budgets, n_items, mw, flags):
+        self.masks = np.zeros((n_seqs, n_budgets, mw), dtype=np.uint64)
+        self.cos = np.zeros((n_seqs, n_budgets), dtype=np.float32)
+        self.valid = np.zeros((n_seqs, n_budgets), dtype=np.uint8)
+        self.t_draft = np.zeros((n_seqs, n_budgets), dtype=np.float64)
+        self.item_weight = np.zeros((n_seqs, n_items), dtype=np.int32)
+        self.best_budget = np.zeros(n_seqs, dtype=np.int32)
+        self.best_gamma = np.zeros(n_seqs, dtype=np.int32)
+        self.best_tpt = np.zeros(n_seqs, dtype=np.float64)
+        self.decisions = (np.zeros((n_seqs, n_items, n_budgets), dtype=np.uint8)
+                          if flags & KNAPSPEC_RETURN_DECISIONS else None)
+        self.margins = (np.zeros((n_seqs, n_items, n_budgets), dtype=np.float32)
+                        if flags & KNAPSPEC_RETURN_MARGINS else None)
+        self.struct = knapspec_result(
+            _ptr(self.masks, C.c_uint64), _ptr(self.cos, C.c_float), _ptr(self.valid, C.c_uint8),
+            _ptr(self.t_draft, C.c_double), _ptr(self.item_weight, C.c_int32),
+            _ptr(self.best_budget, C.c_int32), _ptr(self.best_gamma, C.c_int32),
+            _ptr(self.best_tpt, C.c_double),
+            _ptr(self.decisions, C.c_uint8) if self.decisions is not None else None,
+            _ptr(self.margins, C.c_float) if self.margins is not None else None)
+
+
+class Model:
+    """Owns a knapspec_model handle built from torch device tensors (kept alive here)."""
+
+    def __init__(self, desc: dict, layers: Sequence[dict], stream=None):
+        import torch
+
+        self._torch = torch
+        self.desc = knapspec_model_desc(**desc)
+        self.n_layers = self.desc.n_layers
+        self.mw = int(knapspec_mask_words(self.n_layers))
+        self._layers = list(layers)  # keep tensors alive
+        arr = (knapspec_layer_weights * self.n_layers)()
+        for i, lw in enumerate(layers):
+            arr[i] = knapspec_layer_weights(lw["w_qkv"].data_ptr(), lw["w_o"].data_ptr(),
+                                            lw["w_gate_up"].data_ptr(), lw["w_down"].data_ptr())
+        h = C.c_void_p()
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(knapspec_load_model(C.byref(self.desc), arr, C.c_void_p(s), C.byref(h)),
+               "knapspec_load_model")
+        self.handle = h
+
+    def set_latency(self, attn_base, attn_per_token, mlp, fixed=0.0, per_item=None):
+        lat, keep = latency_struct(attn_base, attn_per_token, mlp, fixed, per_item)
+        _check(knapspec_set_latency_model(self.handle, C.byref(lat)),
+               "knapspec_set_latency_model")
+
+    def solve(self, seqs: List[dict], n_budgets: int, gamma, tau: float = -math.inf,
+              max_skip_weight: int = -1, flags: int = 0, stream=None,
+              result: Optional[Result] = None) -> Result:
+        """seqs: dicts with ctx (int), k_cache / v_cache (lists of device tensors per layer,
+        [hkv][capacity][dh]), x0 (device float32 [d])."""
+        torch = self._torch
+        S = len(seqs)
+        carr = (knapspec_seq * S)()
+        keep = []
+        for i, sq in enumerate(seqs):
+            kp = (C.c_void_p * self.n_layers)(*[t.data_ptr() for t in sq["k_cache"]])
+            vp = (C.c_void_p * self.n_layers)(*[t.data_ptr() for t in sq["v_cache"]])
+            keep += [kp, vp]
+            cap = int(sq["k_cache"][0].shape[1]) if self.n_layers else 0
+            carr[i] = knapspec_seq(int(sq["ctx"]), cap, C.cast(kp, C.POINTER(C.c_void_p)),
+                                   C.cast(vp, C.POINTER(C.c_void_p)), sq["x0"].data_ptr())
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        args = knapspec_solve_args(S, carr, int(n_budgets), int(gamma[0]), int(gamma[1]),
+                                   float(tau), int(max_skip_weight), int(flags), C.c_void_p(s))
+        res = result if result is not None else Result(S, n_budgets, 2 * self.n_layers, self.mw,
+                                                        flags)
+        _check(knapspec_solve(self.handle, C.byref(args), C.byref(res.struct)), "knapspec_solve")
+        return res
+
+    def set_profiling(self, enable: bool):
+        _check(knapspec_set_profiling(self.handle, 1 if enable else 0), "knapspec_set_profiling")
+
+    def kernel_times(self) -> dict:
+        n = len(KERNEL_CLASSES)
+        ms = (C.c_double * n)()
+        cnt = (C.c_int64 * n)()
+        _check(knapspec_get_kernel_times(self.handle, ms, cnt, n), "knapspec_get_kernel_times")
+        return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
+
+    def close(self):
+        if getattr(self, "handle", None):
+            knapspec_free_model(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,193 @@
+/*
+ * knapspec.h -- C ABI of the MI355X (gfx950) KnapSpec layer-selection library.
+ *
+ * What it computes.  KnapSpec (Cha, Kim, Han, Yang, Han; arXiv 2602.20217, described on the
+ * pith.science review page) treats each Attention and each MLP block of a decoder as a 0/1
+ * knapsack item.  An item's weight is its latency (Attention grows linearly with the context
+ * length, MLP is flat: review, "The reading"); its value is how close the hidden state stays
+ * to the full model's, measured by cosine similarity.  A dynamic program over items x latency
+ * budgets keeps, at every item and budget, whichever of "execute" or "skip" gives the higher
+ * cosine to the full model's state at that depth (review, "What carries the argument";
+ * referee major comment 1: Section 3.4, Eq. 8, Algorithm 1), giving one candidate layer set
+ * per budget.  A grid over the draft length gamma then maximises Tokens-per-Time,
+ *     TPT(S, gamma) = ((1 - a^(gamma+1)) / (1 - a)) / (gamma * t_draft(S) + t_target)
+ * (review, "What carries the argument", Eq. 4), where a is the acceptance estimate of S.
+ *
+ * Conventions used by every call:
+ *   - Items i = 0 .. 2L-1: item 2l is the Attention block of layer l, item 2l+1 its MLP.
+ *   - Budget b = 0 .. n_budgets-1 is the USED integer weight sum over executed items.  The
+ *     paper indexes by skipped weight j; the two are related by b = P_i - j with P_i the
+ *     weight prefix sum through item i (review, referee minor comment 2).
+ *   - Weights: Delta = (sum of item latencies) / (n_budgets - 1) and
+ *     w_i = max(1, round-half-even(t_i / Delta)) (review, referee major comment 4: w = t/Delta).
+ *   - The decoder is a Llama-style pre-norm block: RMSNorm (unit gain) -> q|k|v projection
+ *     -> rotate-half RoPE at position ctx_len -> grouped-query softmax attention over the
+ *     ctx_len cached positions plus the token's own k/v -> output projection + residual;
+ *     RMSNorm -> gate|up projection -> silu(gate)*up -> down projection + residual.
+ *   - Exact cosine ties keep "skip"; a NaN cosine counts as minus infinity.
+ *
+ * Error behaviour: every int-returning call returns KNAPSPEC_OK (0) or a negative code and
+ * never throws or aborts; the message of the last failure on the calling thread is
+ * available from knapspec_last_error().  On failure, outputs are left untouched.
+ * Threading: a model handle must not be used by two threads at once.
+ */
+#ifndef KNAPSPEC_H
+#define KNAPSPEC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KNAPSPEC_ABI_VERSION 1
+
+#define KNAPSPEC_OK 0
+#define KNAPSPEC_EINVAL (-1)       /* bad argument, shape or pointer */
+#define KNAPSPEC_ENOMEM (-2)       /* a device or pinned-host allocation failed */
+#define KNAPSPEC_EHIP (-3)         /* HIP runtime or kernel launch error */
+#define KNAPSPEC_EUNSUPPORTED (-4) /* a shape the compiled kernels do not cover */
+
+#define KNAPSPEC_F32 0  /* weights and KV cache in float32 */
+#define KNAPSPEC_BF16 1 /* weights and KV cache in bfloat16 */
+
+#define KNAPSPEC_RETURN_DECISIONS 1 /* fill knapspec_result.decisions */
+#define KNAPSPEC_RETURN_MARGINS 2   /* fill knapspec_result.margins */
+
+typedef struct knapspec_model knapspec_model; /* opaque */
+
+/* Decoder shape and the limits the library sizes its device workspace for. */
+typedef struct {
+  int32_t n_layers;    /* L; the DP has 2L items */
+  int32_t d_model;     /* hidden size d */
+  int32_t n_q_heads;   /* hq */
+  int32_t n_kv_heads;  /* hkv, divides hq; query head h reads KV head h / (hq/hkv) */
+  int32_t head_dim;    /* dh (64 or 128 for bf16; any even value <= 128 for f32) */
+  int32_t d_ff;        /* SwiGLU inner size */
+  int32_t dtype;       /* KNAPSPEC_F32 or KNAPSPEC_BF16 */
+  float rms_eps;       /* RMSNorm epsilon */
+  float rope_theta;    /* RoPE base: angle_j = pos * theta^(-2j/dh) */
+  int32_t max_budgets; /* largest n_budgets a solve may use (2..1024) */
+  int32_t max_seqs;    /* largest n_seqs a solve may use */
+  int32_t max_ctx;     /* largest ctx_len a solve may use */
+} knapspec_model_desc;
+
+/* Device pointers of one layer's weights, row-major [out][in], in desc.dtype:
+ *   w_qkv     [(hq + 2*hkv) * dh][d]   rows: q heads, then k heads, then v heads
+ *   w_o       [d][hq * dh]
+ *   w_gate_up [2 * d_ff][d]            rows: gate, then up
+ *   w_down    [d][d_ff]
+ * Borrowed: the caller keeps them alive and unchanged until knapspec_free_model. */
+typedef struct {
+  const void *w_qkv, *w_o, *w_gate_up, *w_down;
+} knapspec_layer_weights;
+
+/* Validates the shape, records the weight pointers and allocates the device workspace
+ * (sized from max_budgets, max_seqs and max_ctx) and pinned host staging.  hip_stream is
+ * the stream used for set-up work (NULL = default stream).  *out receives the handle. */
+int knapspec_load_model(const knapspec_model_desc* desc, const knapspec_layer_weights* layers,
+                        void* hip_stream, knapspec_model** out);
+
+/* Per-item latency model (one-time profile; review, "Editorial extensions": profiling once,
+ * re-solving on the fly).  t_attn(n) = attn_base + attn_per_token * n, t_mlp = mlp, and
+ * `fixed` is added once to every pass (draft and target).  per_item, when not NULL, points to
+ * 2L host doubles that replace the linear model for every sequence (copied).  All values must
+ * be finite and >= 0, with a positive total.  Until this is called, solves fail (EINVAL). */
+typedef struct {
+  double attn_base, attn_per_token, mlp, fixed;
+  const double* per_item;
+} knapspec_latency_model;
+
+int knapspec_set_latency_model(knapspec_model* model, const knapspec_latency_model* lat);
+
+/* One sequence to solve for.  All pointers are device pointers borrowed for the call.
+ *   k_cache[l], v_cache[l]: layer l's cache, [hkv][ctx_capacity][dh] in desc.dtype, holding
+ *     positions 0 .. ctx_len-1 already rotated; the new token sits at position ctx_len.
+ *   x0: float32 [d], the new token's input hidden state. */
+typedef struct {
+  int32_t ctx_len;      /* 0 .. max_ctx */
+  int32_t ctx_capacity; /* positions per KV head in the buffers, >= ctx_len */
+  const void* const* k_cache; /* host array of n_layers device pointers */
+  const void* const* v_cache; /* host array of n_layers device pointers */
+  const float* x0;
+} knapspec_seq;
+
+typedef struct {
+  int32_t n_seqs;             /* 1 .. max_seqs; sequences are solved together, independently */
+  const knapspec_seq* seqs;   /* host array [n_seqs] */
+  int32_t n_budgets;          /* B, 2 .. max_budgets */
+  int32_t gamma_min, gamma_max; /* TPT grid, 1 <= gamma_min <= gamma_max <= 64 */
+  float tau;                  /* prune a cell whose kept cosine < tau; -INFINITY disables */
+  int32_t max_skip_weight;    /* prune cells whose skipped weight P_i - b exceeds it; <0 off */
+  int32_t flags;              /* KNAPSPEC_RETURN_DECISIONS | KNAPSPEC_RETURN_MARGINS */
+  void* hip_stream;           /* stream the work is enqueued on (NULL = default stream) */
+} knapspec_solve_args;
+
+/* Caller-allocated HOST arrays; "W" = knapspec_mask_words(n_layers), L2 = 2 * n_layers. */
+typedef struct {
+  uint64_t* masks;      /* [n_seqs][n_budgets][W]; bit i of word i/64 set = item i executed */
+  float* cos;           /* [n_seqs][n_budgets] cosine to the full model after item 2L-1; NaN
+                           where invalid */
+  uint8_t* valid;       /* [n_seqs][n_budgets] 1 = budget holds a candidate set */
+  double* t_draft;      /* [n_seqs][n_budgets] fixed + sum of t_i over executed items */
+  int32_t* item_weight; /* [n_seqs][L2] integer weights used */
+  int32_t* best_budget; /* [n_seqs] argmax budget of the TPT grid, -1 if none valid */
+  int32_t* best_gamma;  /* [n_seqs] its gamma, -1 if none valid */
+  double* best_tpt;     /* [n_seqs] its TPT, NaN if none valid */
+  uint8_t* decisions;   /* nullable [n_seqs][L2][n_budgets]: 0 skip, 1 execute, 255 invalid */
+  float* margins;       /* nullable [n_seqs][L2][n_budgets]: |c_exec - c_skip|, +inf when one
+                           option exists, NaN when none */
+} knapspec_result;
+
+/* Runs the whole DP for every sequence on the GPU: per item, one batched GEMM over all live
+ * budget rows of all sequences (plus each sequence's full-model reference row), attention that
+ * streams each layer's KV cache once per sequence for all rows, and the per-budget
+ * cosine/select.  Enqueues on args->hip_stream, synchronises once, copies the per-budget
+ * results to `result` and runs the TPT grid on the host with a = clamp(cos, 0, 1).
+ * The acceptance proxy a = clamp(cos) stands in for the paper's history estimate (Eq. 9),
+ * which the pages do not print. */
+int knapspec_solve(knapspec_model* model, const knapspec_solve_args* args,
+                   knapspec_result* result);
+
+/* Host-only TPT grid for caller-supplied acceptance estimates alpha[b] (any a in [0,1]).
+ * Ties keep the smaller budget, then the smaller gamma.  Writes -1/-1/NaN when no budget is
+ * valid.  Needs no GPU. */
+int knapspec_tpt_select(const float* alpha, const double* t_draft, const uint8_t* valid,
+                        int32_t n_budgets, double t_target, int32_t gamma_min,
+                        int32_t gamma_max, int32_t* best_budget, int32_t* best_gamma,
+                        double* best_tpt);
+
+/* Host-only: the latencies t_i and integer weights w_i one solve uses for a sequence at
+ * context length ctx_len (t: 2L doubles, w: 2L int32; either may be NULL).  Needs no GPU. */
+int knapspec_item_weights(const knapspec_latency_model* lat, int32_t n_layers, int32_t ctx_len,
+                          int32_t n_budgets, double* t, int32_t* w);
+
+/* Measurement hook.  With profiling enabled, knapspec_solve brackets every kernel launch with
+ * a pair of HIP events on the solve stream and, after its synchronisation, adds the elapsed
+ * time to one of the kernel classes below.  Enabling (enable = 1) resets the counters;
+ * knapspec_get_kernel_times copies them (n_classes entries, at most KNAPSPEC_KERNEL_CLASSES).
+ * Profiling adds two event records per launch and does not change any result. */
+#define KNAPSPEC_KERNEL_CLASSES 9
+#define KNAPSPEC_K_INIT 0
+#define KNAPSPEC_K_GEMM_QKV 1
+#define KNAPSPEC_K_QKV_ROPE 2
+#define KNAPSPEC_K_ATTENTION 3
+#define KNAPSPEC_K_COMBINE 4
+#define KNAPSPEC_K_GEMM_O 5
+#define KNAPSPEC_K_GEMM_GATE_UP 6
+#define KNAPSPEC_K_GEMM_DOWN 7
+#define KNAPSPEC_K_SELECT 8
+int knapspec_set_profiling(knapspec_model* model, int32_t enable);
+int knapspec_get_kernel_times(const knapspec_model* model, double* total_ms, int64_t* launches,
+                              int32_t n_classes);
+
+int32_t knapspec_mask_words(int32_t n_layers); /* ceil(2L / 64) */
+void knapspec_free_model(knapspec_model* model); /* NULL is a no-op */
+const char* knapspec_last_error(void);          /* thread-local; "" when none */
+int32_t knapspec_abi_version(void);             /* KNAPSPEC_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KNAPSPEC_H */
