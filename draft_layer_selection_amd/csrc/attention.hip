@@ -139,14 +139,26 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// MFMA attention partial (bf16, dh = 128): 4 waves x 32 query rows, 64-key tiles in LDS.
+// MFMA attention partial (bf16, dh = 128): 4 waves x 32 query rows, 64-key tiles.
+//   * the next tile's K/V are loaded into registers while the current tile is computed,
+//     then written to the other LDS buffer: one barrier per tile;
+//   * threads 0..127 stage K rows as they are ([key][dh]); threads 128..255 each load an
+//     8-key x 8-dh block of V, transpose it in registers and store 8-key rows of V^T, so the
+//     P.V MFMA reads its operand with 8-byte LDS loads;
+//   * softmax in the log2 domain on raw scores: p = exp2(s*c - m*c), c = log2(e)/sqrt(dh);
+//     the O rescale is skipped when no lane's running max moved.
 // ------------------------------------------------------------------------------------
 constexpr int DHM = 128;
 constexpr int KT = 64;            // keys per tile
 constexpr int K_PITCH = DHM + 8;  // LDS row pitch of K [key][dh] (bf16 elements)
 constexpr int V_PITCH = KT + 8;   // LDS row pitch of V^T [dh][key]
 
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const int4 wk = a.work[blockIdx.x];
   const AttnSeq S = a.seqs[wk.x];
   const int c = wk.y, qb = wk.z, sp = wk.w;
@@ -161,6 +173,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   const int h = c * G + tt % G;
   const int k0 = sp * S.chunk;
   const int k1 = min(S.ctx, k0 + S.chunk);
+  const float cs = a.scale_log2;
 
   // this lane's query row as the B operand of S^T = K Q^T: 8 K-steps of 16 dh
   const bf16* qp = (const bf16*)a.Q + ((size_t)row * a.hq + h) * DHM + hi * 8;
@@ -168,8 +181,60 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
 
-  __shared__ bf16 Ks[KT * K_PITCH];
-  __shared__ bf16 Vt[DHM * V_PITCH];
+  __shared__ bf16 Ks[2][KT * K_PITCH];
+  __shared__ bf16 Vt[2][DHM * V_PITCH];
+
+  const bf16* kbase = (const bf16*)S.k + (size_t)c * S.cap * DHM;
+  const bf16* vbase = (const bf16*)S.v + (size_t)c * S.cap * DHM;
+  const bool k_role = tid < 128;
+  const int u = tid & 127;
+  bf16x8 stg[8];
+  bf16x8 zero8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zero8[e] = (bf16)0.f;
+
+  auto load_tile = [&](int kt) {
+    if (k_role) {
+      const int key = kt + (u >> 1);
+      const bf16* src = kbase + (size_t)key * DHM + (u & 1) * 64;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) stg[e] = key < k1 ? *(const bf16x8*)(src + 8 * e) : zero8;
+    } else {
+      const int kb8 = u & 7, j = u >> 3;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int key = kt + 8 * kb8 + r;
+        stg[r] = key < k1 ? *(const bf16x8*)(vbase + (size_t)key * DHM + 8 * j) : zero8;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if (k_role) {
+      bf16* dst = &Ks[buf][(u >> 1) * K_PITCH + (u & 1) * 64];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *(bf16x8*)(dst + 8 * e) = stg[e];
+    } else {
+      // stg[r] holds V[key 8*kb8 + r][dh 8j .. 8j+7]; word k of it = dh pair (2k, 2k+1).
+      // Column cc of the block (dh 8j + cc) as 8 keys: word m = (V[2m][cc], V[2m+1][cc]).
+      const int kb8 = u & 7, j = u >> 3;
+      u32x4 w[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) w[r] = as_u32x4(stg[r]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          u32x4 col;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const unsigned lo = w[2 * m][k], hw = w[2 * m + 1][k];
+            col[m] = b == 0 ? ((lo & 0xFFFFu) | (hw << 16)) : ((lo >> 16) | (hw & 0xFFFF0000u));
+          }
+          *(u32x4*)(&Vt[buf][(8 * j + 2 * k + b) * V_PITCH + 8 * kb8]) = col;
+        }
+      }
+    }
+  };
 
   f32x16 o[4];
 #pragma unroll
@@ -178,31 +243,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  const bf16* kbase = (const bf16*)S.k + (size_t)c * S.cap * DHM;
-  const bf16* vbase = (const bf16*)S.v + (size_t)c * S.cap * DHM;
-
+  int buf = 0;
+  if (k0 < k1) {
+    load_tile(k0);
+    store_tile(0);
+  }
+  __syncthreads();
   for (int kt = k0; kt < k1; kt += KT) {
-    // stage 64 keys x 128 dh of K (row-major) and V (transposed) into LDS
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * 256 + tid;
-      const int key = idx >> 4, dc = (idx & 15) * 8;
-      bf16x8 kv, vv;
-      if (kt + key < k1) {
-        kv = *(const bf16x8*)(kbase + (size_t)(kt + key) * DHM + dc);
-        vv = *(const bf16x8*)(vbase + (size_t)(kt + key) * DHM + dc);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kv[e] = (bf16)0.f;
-          vv[e] = (bf16)0.f;
-        }
-      }
-      *(bf16x8*)(&Ks[key * K_PITCH + dc]) = kv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(dc + e) * V_PITCH + key] = vv[e];
-    }
-    __syncthreads();
+    const bool more = kt + KT < k1;
+    if (more) load_tile(kt + KT);
 
     // scores: two 32-key blocks; lane holds query l32, keys 8*(r/4) + 4*hi + r%4
     f32x16 sacc[2];
@@ -212,29 +261,37 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(&Ks[(kb * 32 + l32) * K_PITCH + ks * 16 + hi * 8]);
+        const bf16x8 kf =
+            *(const bf16x8*)(&Ks[buf][(kb * 32 + l32) * K_PITCH + ks * 16 + hi * 8]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-    float mt = -INFINITY;
+    if (kt + KT > k1) {  // ragged last tile (uniform branch)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float sv = key < k1 ? sacc[kb][r] * a.scale_log2 : -INFINITY;
-        sacc[kb][r] = sv;
-        mt = fmaxf(mt, sv);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= k1) sacc[kb][r] = -INFINITY;
+        }
     }
+    float mt = sacc[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[1][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float mn = fmaxf(m, mt);
-    const float corr = exp2f(m - mn);
-    lsum *= corr;
+    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {  // some running max moved: rescale
+      const float corr = exp2f((m - mn) * cs);
+      lsum *= corr;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+        for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+    }
+    m = mn;
+    const float mc = mn * cs;
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -243,26 +300,25 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(sacc[kb][8 * st + e] - mn);
+          const float p = exp2f(fmaf(sacc[kb][8 * st + e], cs, -mc));
           lsum += p;
           pf[e] = (bf16)p;
         }
         // V^T operand: keys kb*32 + 16*st + 8*(e/4) + 4*hi + e%4 for e = 0..7
-        const int kbase2 = kb * 32 + 16 * st + 4 * hi;
+        const int kofs = kb * 32 + 16 * st + 4 * hi;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16* vrow = &Vt[(db * 32 + l32) * V_PITCH + kbase2];
+          const bf16* vrow = &Vt[buf][(db * 32 + l32) * V_PITCH + kofs];
           const bf16x4 lo = *(const bf16x4*)(vrow);
           const bf16x4 hv = *(const bf16x4*)(vrow + 8);
-          bf16x8 vf;
-          vf[0] = lo[0]; vf[1] = lo[1]; vf[2] = lo[2]; vf[3] = lo[3];
-          vf[4] = hv[0]; vf[5] = hv[1]; vf[6] = hv[2]; vf[7] = hv[3];
+          const bf16x8 vf = __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
         }
       }
     }
-    m = mn;
+    if (more) store_tile(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
   lsum += __shfl_xor(lsum, 32, 64);
   if (!tvalid) return;
@@ -283,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
     }
   }
   if (hi == 0) {
-    a.Mpart[slot] = m;
+    a.Mpart[slot] = m * cs;  // log2 domain, like the combine kernel expects
     a.Lpart[slot] = lsum;
   }
 }

@@ -2,13 +2,23 @@
 // reference rows) multiply one layer's weight matrix, so every weight byte is read from HBM
 // once per item however many budgets are live (the batching of all budgets into one GEMM).
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16):
-//   workgroup = 4 waves, tile = (32*MB rows) x (64 output columns); the 4 waves split each
-//   64-wide K step (16 K each), so every weight element is loaded by exactly one lane of one
-//   wave straight into registers and every activation element once per tile; the four partial
-//   accumulators are summed through LDS in a fixed order (deterministic).  K is split across
-//   workgroups only as far as needed to fill the 256 CUs; the consumer adds the splits.
+// bf16 main path (gemm_lds_kernel, gfx950 MFMA v_mfma_f32_32x32x16_bf16):
+//   * workgroup = 8 waves = NG column groups (64 output columns each) x (8/NG) K slices;
+//     tile = 64*NG columns x 32*MB rows; one workgroup per CU (the LDS ring takes ~128-144 KB);
+//   * weights and activations go global -> LDS with global_load_lds_dwordx4 (no registers),
+//     8 lanes per 128-byte row segment, in a ring of S stages of 64 K each, so S-1 stages are
+//     in flight; 16-byte slots are XOR-swizzled by row so the MFMA-layout reads are
+//     bank-conflict free;
+//   * the barrier between stages is a bare s_barrier: each wave first waits (vmcnt) for its own
+//     loads of the stage, and a fenced barrier would instead drain every load in flight;
+//   * activations are re-read from L2 once per column tile, i.e. R/(64*NG) times the weight
+//     bytes, so the planner widens the tile (NG=4) when R > 128;
+//   * K-slice partial sums are reduced through LDS in a fixed order (deterministic); K is split
+//     across workgroups only to fill the 256 CUs, and the consumer adds the splits.
+// bf16 fallback (gemm_bf16_kernel): direct-to-register loads, 64-column tiles, any N % 64 == 0.
 // f32 path: plain LDS-tiled FMA kernel (the small float32 decoder only).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -53,7 +63,9 @@ __device__ __forceinline__ void store_block(const GemmArgs& a, float (*red)[32][
   }
 }
 
-template <int MB>
+// PF = k-steps whose loads are in flight ahead of the MFMAs (register ring buffer): with one
+// step in flight a wave waits a full HBM round trip per 64-wide K step.
+template <int MB, int PF>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int total = a.n_tiles * a.m_tiles * a.splits;
   const int L = xcd_tile(blockIdx.x, a.per_xcd);
@@ -75,7 +87,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     wrow0 = nt * 64 + l32;
     wrow1 = nt * 64 + 32 + l32;
   }
-  const int koff = wave * 16 + hi * 8;
+  const int k0 = sp * a.k_chunk;
+  const int k1 = min(a.K, k0 + a.k_chunk);
+  const int koff = k0 + wave * 16 + hi * 8;
   const bf16* W = (const bf16*)a.W;
   const bf16* w0p = W + (size_t)wrow0 * a.K + koff;
   const bf16* w1p = W + (size_t)wrow1 * a.K + koff;
@@ -87,8 +101,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     r = r < a.R ? r : a.R - 1;
     ap[mb] = A + (size_t)r * a.lda + koff;
   }
-  const int k0 = sp * a.k_chunk;
-  const int k1 = min(a.K, k0 + a.k_chunk);
+  const int nit = (k1 - k0) / 64;
 
   f32x16 acc[MB][2];
 #pragma unroll
@@ -100,17 +113,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
 
-#pragma unroll 2
-  for (int k = k0; k < k1; k += 64) {
-    const bf16x8 b0 = *(const bf16x8*)(w0p + k);
-    const bf16x8 b1 = *(const bf16x8*)(w1p + k);
-    bf16x8 av[MB];
+  bf16x8 wq[PF][2];
+  bf16x8 aq[PF][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) av[mb] = *(const bf16x8*)(ap[mb] + k);
+  for (int p = 0; p < PF; ++p) {
+    if (p < nit) {
+      wq[p][0] = *(const bf16x8*)(w0p + p * 64);
+      wq[p][1] = *(const bf16x8*)(w1p + p * 64);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], b0, acc[mb][0], 0, 0, 0);
-      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], b1, acc[mb][1], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb) aq[p][mb] = *(const bf16x8*)(ap[mb] + p * 64);
+    }
+  }
+  for (int it = 0; it < nit; it += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (it + p < nit) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[p][mb], wq[p][0], acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[p][mb], wq[p][1], acc[mb][1], 0, 0, 0);
+        }
+        const int nx = it + p + PF;
+        if (nx < nit) {
+          wq[p][0] = *(const bf16x8*)(w0p + nx * 64);
+          wq[p][1] = *(const bf16x8*)(w1p + nx * 64);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) aq[p][mb] = *(const bf16x8*)(ap[mb] + nx * 64);
+        }
+      }
     }
   }
 
@@ -128,6 +158,173 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     }
     __syncthreads();
     store_block<bf16>(a, red, row0 + 32 * mb, nt, sp);
+    __syncthreads();
+  }
+}
+
+// s_waitcnt with vmcnt = n (<= 47) and no wait on the other counters (gfx9 encoding).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define KS_WAITVM(N)                                                                        \
+  case N:                                                                                   \
+    __builtin_amdgcn_s_waitcnt(((N)&15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14));       \
+    break;
+    KS_WAITVM(0) KS_WAITVM(1) KS_WAITVM(2) KS_WAITVM(3) KS_WAITVM(4) KS_WAITVM(5)
+    KS_WAITVM(6) KS_WAITVM(7) KS_WAITVM(8) KS_WAITVM(9) KS_WAITVM(10) KS_WAITVM(11)
+    KS_WAITVM(12) KS_WAITVM(13) KS_WAITVM(14) KS_WAITVM(15) KS_WAITVM(16) KS_WAITVM(17)
+    KS_WAITVM(18) KS_WAITVM(19) KS_WAITVM(20) KS_WAITVM(21) KS_WAITVM(22) KS_WAITVM(23)
+    KS_WAITVM(24) KS_WAITVM(25) KS_WAITVM(26) KS_WAITVM(27) KS_WAITVM(28) KS_WAITVM(29)
+    KS_WAITVM(30) KS_WAITVM(31) KS_WAITVM(32) KS_WAITVM(33) KS_WAITVM(34) KS_WAITVM(35)
+    KS_WAITVM(36) KS_WAITVM(37) KS_WAITVM(38) KS_WAITVM(39) KS_WAITVM(40)
+#undef KS_WAITVM
+    default:
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+      break;
+  }
+}
+
+template <int NG, int MB, int S>
+__global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
+  constexpr int KSL = 8 / NG;          // K slices (waves per column group)
+  constexpr int KSTEPS = 4 / KSL;      // 16-wide K steps per wave per 64-K stage
+  constexpr int WR = 64 * NG;          // weight rows per stage
+  constexpr int ROWS = WR + 32 * MB;   // + activation rows
+  constexpr int STAGE = ROWS * 128;    // bytes per stage (64 bf16 of K per row)
+  constexpr int NCH = ROWS / 8;        // 1 KB chunks (8 rows) per stage
+  constexpr int PER_WAVE = (NCH + 7) / 8;
+  constexpr int RP = 64 * NG + 4;      // reduction buffer pitch (floats)
+  static_assert(KSL * 32 * RP * 4 <= S * STAGE, "reduction buffer must fit in the ring");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
+
+  const int total = a.n_tiles * a.m_tiles * a.splits;
+  const int L = xcd_tile(blockIdx.x, a.per_xcd);
+  if (L >= total) return;
+  const int mt = L % a.m_tiles;
+  const int rest = L / a.m_tiles;
+  const int sp = rest % a.splits;
+  const int nt = rest / a.splits;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int grp = wave / KSL, ksl = wave % KSL;
+  const int row0 = mt * 32 * MB;
+  const int k0 = sp * a.k_chunk;
+  const int k1 = min(a.K, k0 + a.k_chunk);
+  const int nit = (k1 - k0) / 64;
+  const bf16* W = (const bf16*)a.W;
+  const bf16* A = (const bf16*)a.A;
+
+  // Loader: chunk q = 8 stage rows; lane -> row 8q + lane/8, LDS slot lane%8 which holds the
+  // row's global 16-byte chunk (lane%8) ^ (row%8).
+  const bf16* src[PER_WAVE];
+  const int rin = lane >> 3;
+  const int cglob = (lane & 7) ^ rin;
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int q = wave + 8 * j;
+    const int r = 8 * q + rin;
+    if (q >= NCH) {
+      src[j] = W;
+    } else if (r < WR) {
+      int wrow;
+      if (a.mode == GEMM_SWIGLU)
+        wrow = r < WR / 2 ? nt * (WR / 2) + r : a.ff + nt * (WR / 2) + (r - WR / 2);
+      else
+        wrow = nt * WR + r;
+      src[j] = W + (size_t)wrow * a.K + k0 + 8 * cglob;
+    } else {
+      int ar = row0 + (r - WR);
+      ar = ar < a.R ? ar : a.R - 1;
+      src[j] = A + (size_t)ar * a.lda + k0 + 8 * cglob;
+    }
+  }
+  const int my_loads = (NCH - wave + 7) / 8;  // chunks this wave issues per stage
+  auto issue = [&](int stage, int slot) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int q = wave + 8 * j;
+      if (q < NCH)
+        __builtin_amdgcn_global_load_lds((const void*)(src[j] + stage * 64),
+                                         (void*)(smem + slot * STAGE + q * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[mb][0][r] = 0.f;
+      acc[mb][1][r] = 0.f;
+    }
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < nit) issue(p, p);
+
+  for (int it = 0; it < nit; ++it) {
+    wait_vmcnt(min(S - 2, nit - 1 - it) * my_loads);  // this wave's part of stage `it` landed
+    asm volatile("s_barrier" ::: "memory");            // ... and everyone else's
+    if (it + S - 1 < nit) issue(it + S - 1, (it + S - 1) % S);  // refill the slot freed above
+    const unsigned char* st = smem + (it % S) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int c = 2 * (ksl * KSTEPS + ks) + hi;  // 16-byte chunk of this lane's K
+      bf16x8 wf[2], af[MB];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int r = 64 * grp + 32 * cb + l32;
+        wf[cb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ (r & 7)));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = WR + 32 * mb + l32;
+        af[mb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ (r & 7)));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], wf[0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], wf[1], acc[mb][1], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+
+  float (*red)[32][RP] = (float (*)[32][RP])smem;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (row0 + 32 * mb >= a.R) break;  // uniform across the workgroup
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        red[ksl][8 * (r >> 2) + 4 * hi + (r & 3)][64 * grp + 32 * cb + l32] = acc[mb][cb][r];
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (a.mode == GEMM_PARTIAL) {
+      for (int e = tid; e < 32 * WR; e += 512) {
+        const int r = e / WR, cc = e % WR;
+        const int grow = row0 + 32 * mb + r;
+        if (grow >= a.R) continue;
+        float v = red[0][r][cc];
+#pragma unroll
+        for (int k = 1; k < KSL; ++k) v += red[k][r][cc];
+        a.P[((size_t)sp * a.R + grow) * a.ldp + nt * WR + cc] = v;
+      }
+    } else {
+      bf16* H = (bf16*)a.H;
+      constexpr int HW = WR / 2;
+      for (int e = tid; e < 32 * HW; e += 512) {
+        const int r = e / HW, j = e % HW;
+        const int grow = row0 + 32 * mb + r;
+        if (grow >= a.R) continue;
+        float g = red[0][r][j], u = red[0][r][HW + j];
+#pragma unroll
+        for (int k = 1; k < KSL; ++k) {
+          g += red[k][r][j];
+          u += red[k][r][HW + j];
+        }
+        H[(size_t)grow * a.ldh + nt * HW + j] = (bf16)(silu_f(g) * u);
+      }
+    }
     __syncthreads();
   }
 }
@@ -212,19 +409,73 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 }  // namespace
 
+GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_floats) {
+  GemmPlan p{};
+  const int ncols = mode == GEMM_SWIGLU ? 2 * ff : N;
+  if (act == ACT_F32) {
+    p.ng = 0;
+    p.mb = 1;
+    p.m_tiles = (R + 31) / 32;
+    p.n_tiles = mode == GEMM_SWIGLU ? (ff + 31) / 32 : (N + 63) / 64;
+  } else {
+    p.m_tiles = (R + 127) / 128;
+    p.mb = (R + 32 * p.m_tiles - 1) / (32 * p.m_tiles);
+    const bool k_ok = K % 64 == 0;
+    if (k_ok && R > 128 && ncols % 256 == 0 && (mode != GEMM_SWIGLU || ff % 128 == 0))
+      p.ng = 4;
+    else if (k_ok && ncols % 128 == 0 && (mode != GEMM_SWIGLU || ff % 64 == 0))
+      p.ng = 2;
+    else
+      p.ng = 0;
+    const int cols = p.ng ? 64 * p.ng : 64;
+    p.n_tiles = mode == GEMM_SWIGLU ? ff / (cols / 2) : N / cols;
+  }
+  const int kstep = act == ACT_F32 ? 32 : 64;
+  const int kiters = (K + kstep - 1) / kstep;
+  int s = 1;
+  if (mode != GEMM_SWIGLU) {
+    const int tiles = p.n_tiles * p.m_tiles;
+    const int lds_kernel = p.ng != 0;
+    // one workgroup per CU for the LDS kernel: fill up to 256 without a second round
+    const int target = lds_kernel ? 256 : 512;
+    s = std::max(1, target / std::max(1, tiles));
+    s = std::min(s, 16);
+    s = std::min(s, std::max(1, kiters / 4));
+    while (s > 1 && (size_t)s * R * N > cap_floats) --s;
+  }
+  const int per = (kiters + s - 1) / s;
+  p.k_chunk = per * kstep;
+  p.splits = (kiters + per - 1) / per;
+  return p;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s) {
   const int total = a.n_tiles * a.m_tiles * a.splits;
   GemmArgs b = a;
   b.per_xcd = (total + 7) / 8;
-  const dim3 grid(b.per_xcd * 8), block(256);
+  const dim3 grid(b.per_xcd * 8);
   if (act == ACT_F32) {
-    hipLaunchKernelGGL(gemm_f32_kernel, grid, block, 0, s, b);
+    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, b);
+  } else if (a.ng == 4) {
+    switch (a.mb) {
+      case 1: hipLaunchKernelGGL((gemm_lds_kernel<4, 1, 4>), grid, dim3(512), 0, s, b); break;
+      case 2: hipLaunchKernelGGL((gemm_lds_kernel<4, 2, 3>), grid, dim3(512), 0, s, b); break;
+      case 3: hipLaunchKernelGGL((gemm_lds_kernel<4, 3, 3>), grid, dim3(512), 0, s, b); break;
+      default: hipLaunchKernelGGL((gemm_lds_kernel<4, 4, 3>), grid, dim3(512), 0, s, b); break;
+    }
+  } else if (a.ng == 2) {
+    switch (a.mb) {
+      case 1: hipLaunchKernelGGL((gemm_lds_kernel<2, 1, 7>), grid, dim3(512), 0, s, b); break;
+      case 2: hipLaunchKernelGGL((gemm_lds_kernel<2, 2, 6>), grid, dim3(512), 0, s, b); break;
+      case 3: hipLaunchKernelGGL((gemm_lds_kernel<2, 3, 5>), grid, dim3(512), 0, s, b); break;
+      default: hipLaunchKernelGGL((gemm_lds_kernel<2, 4, 4>), grid, dim3(512), 0, s, b); break;
+    }
   } else {
     switch (a.mb) {
-      case 1: hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, block, 0, s, b); break;
-      case 2: hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, block, 0, s, b); break;
-      case 3: hipLaunchKernelGGL(gemm_bf16_kernel<3>, grid, block, 0, s, b); break;
-      default: hipLaunchKernelGGL(gemm_bf16_kernel<4>, grid, block, 0, s, b); break;
+      case 1: hipLaunchKernelGGL((gemm_bf16_kernel<1, 8>), grid, dim3(256), 0, s, b); break;
+      case 2: hipLaunchKernelGGL((gemm_bf16_kernel<2, 6>), grid, dim3(256), 0, s, b); break;
+      case 3: hipLaunchKernelGGL((gemm_bf16_kernel<3, 5>), grid, dim3(256), 0, s, b); break;
+      default: hipLaunchKernelGGL((gemm_bf16_kernel<4, 4>), grid, dim3(256), 0, s, b); break;
     }
   }
   return hipGetLastError();

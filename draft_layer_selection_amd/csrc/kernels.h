@@ -36,7 +36,14 @@ struct GemmArgs {
   int ldh;
   int ff;
   int per_xcd;    // ceil(total tiles / 8): XCD-aware tile order
+  int ng;         // LDS kernel: 64-column groups per tile (2 or 4); 0 = direct-load kernel
 };
+
+// Tile/split plan of one GEMM launch (chosen on the host, see plan_gemm).
+struct GemmPlan {
+  int ng, mb, m_tiles, n_tiles, splits, k_chunk;
+};
+GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_floats);
 
 // ---------------------------------------------------------------------------------------
 // Attention over the shared KV cache (split over context positions) + combine with self.

@@ -55,6 +55,29 @@ struct Carver {
   }
 };
 
+// Byte offsets of the per-solve map / launch tables (same layout on host and device).
+struct MapLayout {
+  size_t exec, next, rowseq, info, work, aseq, rope, x0, init, total, max_work;
+};
+
+MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int hkv, int G,
+                     int dh, int asplit_max) {
+  MapLayout L{};
+  Carver c;
+  L.exec = c.take((size_t)L2 * S * Bm * 4);
+  L.next = c.take((size_t)L2 * S * Bm * 4);
+  L.rowseq = c.take((size_t)L2 * Rmax * 4);
+  L.info = c.take((size_t)L2 * S * sizeof(ks::ItemSeq));
+  L.max_work = (size_t)n_layers * S * hkv * ((G * Bm + 63) / 64) * asplit_max;
+  L.work = c.take(L.max_work * 16);
+  L.aseq = c.take((size_t)n_layers * S * sizeof(ks::AttnSeq));
+  L.rope = c.take(S * dh * 4);
+  L.x0 = c.take(S * 8);
+  L.init = c.take(S * 2 * 4);
+  L.total = c.off;
+  return L;
+}
+
 }  // namespace
 
 struct knapspec_model {
@@ -337,17 +360,8 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   const size_t o_cos = c.take(S * Bm * 4);
   // row maps and launch tables, rebuilt on the host each solve and uploaded once
   const int G = d.n_q_heads / d.n_kv_heads;
-  const size_t qblocks = (size_t)(G * Bm + 63) / 64;
-  Carver mc;
-  mc.take(2 * (size_t)m->L2 * S * Bm * 4);                                  // exec/next rows
-  mc.take((size_t)m->L2 * R * 4);                                           // row -> seq
-  mc.take((size_t)m->L2 * S * sizeof(ks::ItemSeq));                         // item info
-  mc.take((size_t)d.n_layers * S * d.n_kv_heads * qblocks * ASPLIT_MAX * 16);  // attn work
-  mc.take((size_t)d.n_layers * S * sizeof(ks::AttnSeq));                    // attn seqs
-  mc.take(S * d.head_dim * 4);                                              // rope tables
-  mc.take(S * 8);                                                           // x0 pointers
-  mc.take(S * 2 * 4);                                                       // init rows
-  m->maps_bytes = mc.off;
+  m->maps_bytes = map_layout(m->L2, d.n_layers, S, Bm, R, d.n_kv_heads, G, d.head_dim,
+                             ASPLIT_MAX).total;
   const size_t o_maps = c.take(m->maps_bytes);
   m->ws_bytes = c.off;
 
@@ -480,18 +494,6 @@ struct SeqPlan {
   std::vector<std::vector<int>> src;
 };
 
-int choose_splits(int tiles, int K, int kstep, size_t rows, size_t ncols, size_t cap_floats,
-                  int* k_chunk) {
-  const int kiters = (K + kstep - 1) / kstep;
-  int s = 1;
-  while (tiles * s < 512 && s * 2 <= PSPLIT_MAX && kiters / (s * 2) >= 4 &&
-         (size_t)(s * 2) * rows * ncols <= cap_floats)
-    s *= 2;
-  const int per = (kiters + s - 1) / s;
-  *k_chunk = per * kstep;
-  return (kiters + per - 1) / per;
-}
-
 }  // namespace
 
 KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
@@ -571,19 +573,12 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   }
 
   // ---- build the map/launch tables in pinned host memory
-  Carver mc;
-  const size_t o_exec = mc.take((size_t)L2 * S * Bm * 4);
-  const size_t o_next = mc.take((size_t)L2 * S * Bm * 4);
-  const size_t o_rowseq = mc.take((size_t)L2 * m->Rmax * 4);
-  const size_t o_info = mc.take((size_t)L2 * S * sizeof(ks::ItemSeq));
+  const MapLayout ml = map_layout(L2, d.n_layers, S, Bm, m->Rmax, hkv, G, dh, ASPLIT_MAX);
+  const size_t o_exec = ml.exec, o_next = ml.next, o_rowseq = ml.rowseq, o_info = ml.info,
+               o_work = ml.work, o_aseq = ml.aseq, o_rope = ml.rope, o_x0 = ml.x0,
+               o_init = ml.init, max_work = ml.max_work;
   const size_t qb_rows = ks::attention_qblock(m->act, dh);
-  const size_t max_work = (size_t)d.n_layers * S * hkv * ((G * Bm + 63) / 64) * ASPLIT_MAX;
-  const size_t o_work = mc.take(max_work * 16);
-  const size_t o_aseq = mc.take((size_t)d.n_layers * S * sizeof(ks::AttnSeq));
-  const size_t o_rope = mc.take((size_t)S * dh * 4);
-  const size_t o_x0 = mc.take((size_t)S * 8);
-  const size_t o_init = mc.take((size_t)S * 2 * 4);
-  if (mc.off > m->maps_bytes) return fail(KNAPSPEC_EINVAL, "internal: map tables too large");
+  if (ml.total > m->maps_bytes) return fail(KNAPSPEC_EINVAL, "internal: map tables too large");
   char* hm = m->h_maps;
   int32_t* exec_row = (int32_t*)(hm + o_exec);
   int32_t* next_row = (int32_t*)(hm + o_next);
@@ -676,7 +671,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
 
   hipStream_t st = (hipStream_t)args->hip_stream;
   char* dm = m->maps;
-  HIPCHK(hipMemcpyAsync(dm, hm, mc.off, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(dm, hm, ml.total, hipMemcpyHostToDevice, st));
   const int32_t* d_exec = (const int32_t*)(dm + o_exec);
   const int32_t* d_next = (const int32_t*)(dm + o_next);
   const int32_t* d_rowseq = (const int32_t*)(dm + o_rowseq);
@@ -708,7 +703,6 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   const bool want_dec = (args->flags & KNAPSPEC_RETURN_DECISIONS) != 0;
   const bool want_mar = (args->flags & KNAPSPEC_RETURN_MARGINS) != 0;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
-  const int kstep = m->act == ks::ACT_BF16 ? 64 : 32;
 
   auto gemm = [&](const void* A, int lda, int R, const void* W, int K, int N, int mode,
                   int* splits_out, int kclass) -> int {
@@ -719,24 +713,19 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     g.W = W;
     g.K = K;
     g.N = N;
-    g.n_tiles = (N + 63) / 64;
-    if (m->act == ks::ACT_BF16) {
-      g.m_tiles = (R + 127) / 128;
-      g.mb = (R + 32 * g.m_tiles - 1) / (32 * g.m_tiles);
-    } else {
-      g.m_tiles = (R + 31) / 32;
-      g.mb = 1;
-    }
     g.mode = mode;
+    const ks::GemmPlan p = ks::plan_gemm(m->act, R, N, K, mode, d.d_ff, m->p_floats);
+    g.ng = p.ng;
+    g.mb = p.mb;
+    g.m_tiles = p.m_tiles;
+    g.n_tiles = p.n_tiles;
+    g.splits = p.splits;
+    g.k_chunk = p.k_chunk;
     if (mode == ks::GEMM_SWIGLU) {
-      g.splits = 1;
-      g.k_chunk = K;
       g.H = m->h;
       g.ldh = d.d_ff;
       g.ff = d.d_ff;
-      g.n_tiles = (d.d_ff + 31) / 32;
     } else {
-      g.splits = choose_splits(g.n_tiles * g.m_tiles, K, kstep, R, N, m->p_floats, &g.k_chunk);
       g.P = m->P;
       g.ldp = N;
     }

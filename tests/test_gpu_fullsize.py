@@ -1,0 +1,113 @@
+"""Full-size presets on the GPU, in the launch configuration bench.py times.
+
+The oracle cannot redo a whole Llama-3-8B-shape DP in test time, so each case checks
+  * properties that hold at any size: item weights equal the oracle's; valid budgets are
+    exactly the reachable weight sums; every valid mask's weights sum to its budget; the
+    per-cell decisions walk back to the returned masks; t_draft is the sum of the executed
+    items' latencies; the (b, gamma) pick is the TPT argmax of the returned cosines;
+  * the oracle's DP on a prefix of the items (P1 on those cells, tie-aware);
+  * the oracle's forward of a sample of returned masks (P2: cosine within the band).
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+
+from oracle import knapspec_oracle as ko
+from tests.helpers import decoder_shape
+from tests.parity import clean_cells
+from workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+BETA = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def reachable(w, B):
+    r = np.zeros(B, dtype=bool)
+    r[0] = True
+    for wi in w:
+        nr = r.copy()
+        nr[wi:] |= r[: B - wi]
+        r = nr
+    return r
+
+
+def check_structure(res, q, t, B, gamma, n_items, t_target):
+    w = res.item_weight[q].astype(np.int64)
+    valid = res.valid[q].astype(bool)
+    assert np.array_equal(valid, reachable(w, B))
+    bits = ko.unpack_masks(res.masks[q], n_items)
+    for b in range(B):
+        if valid[b]:
+            assert int(np.sum(w[bits[b]])) == b, b
+            assert res.t_draft[q][b] == pytest.approx(float(np.sum(t[bits[b]])), rel=1e-12)
+        else:
+            assert not bits[b].any()
+    dec = res.decisions[q]
+    for b0 in np.nonzero(valid)[0]:
+        b, got = int(b0), np.zeros(n_items, dtype=bool)
+        for i in range(n_items - 1, -1, -1):
+            assert dec[i][b] in (0, 1)
+            if dec[i][b] == 1:
+                got[i] = True
+                b -= int(w[i])
+        assert b == 0 and np.array_equal(got, bits[b0])
+    c = res.cos[q]
+    assert np.all(c[valid] <= 1.0 + 1e-6) and np.all(np.isnan(c[~valid]))
+    alpha = np.clip(np.nan_to_num(c.astype(np.float64), nan=0.0), 0.0, 1.0)
+    pick = ko.tpt_select(alpha, res.t_draft[q], valid, t_target, gamma[0], gamma[1])
+    assert (pick[0], pick[1]) == (int(res.best_budget[q]), int(res.best_gamma[q]))
+
+
+def check_prefix_and_sample(prob, res, q, wl, prefix_layers, n_sample, rng):
+    s = wl.shape
+    n_items = 2 * s.n_layers
+    beta = BETA[s.dtype]
+    lat = wl.latency
+    t = ko.item_latencies(s.n_layers, prob.ctxs[q], lat.attn_base, lat.attn_per_token, lat.mlp)
+    w = ko.item_weights(t, wl.n_budgets)
+    assert np.array_equal(res.item_weight[q], w.astype(np.int32))
+    check_structure(res, q, t, wl.n_budgets, wl.gamma, n_items, float(np.sum(t)))
+    items = ko.DecoderItems(decoder_shape(wl), prob.host_layers, prob.host_kv[q], prob.ctxs[q])
+    # oracle on the first items: decisions on clean cells must agree
+    k = 2 * prefix_layers
+    t0 = time.time()
+    pre = ko.knapsack_dp(items, k, w[:k], prob.host_x0[q], wl.n_budgets)
+    fake = ko.SolveResult(dp=pre, t=t[:k], w=w[:k], masks=None, t_draft=None, t_target=0,
+                          best_budget=-1, best_gamma=-1, best_tpt=0)
+    clean = clean_cells(fake, beta)
+    mism = int(np.sum((res.decisions[q][:k] != pre.decisions) & clean))
+    print(f"  seq {q}: prefix {k} items in {time.time() - t0:.1f}s, clean {clean.sum()}/"
+          f"{clean.size}, clean mismatches {mism}", flush=True)
+    assert mism == 0
+    # oracle forward of sampled returned masks
+    valid = np.nonzero(res.valid[q])[0]
+    picks = set(rng.choice(valid, size=min(n_sample, len(valid)), replace=False).tolist())
+    picks |= {int(valid[0]), int(valid[-1])}
+    if res.best_budget[q] >= 0:
+        picks.add(int(res.best_budget[q]))
+    picks = sorted(picks)
+    bits = ko.unpack_masks(res.masks[q], n_items)[picks]
+    t0 = time.time()
+    ev = ko.eval_subsets(items, n_items, prob.host_x0[q], bits)
+    err = np.abs(ev - res.cos[q][picks].astype(np.float64))
+    print(f"  seq {q}: P2 on budgets {picks}: max err {err.max():.2e} ({time.time() - t0:.1f}s)",
+          flush=True)
+    assert err.max() <= beta
+
+
+@pytest.mark.timeout(900)
+def test_llama3_8b_32k_full():
+    from workloads.device import DeviceProblem
+
+    wl = WORKLOADS["llama3_8b_32k"]
+    print(f"\n[case] {wl.name} full size", flush=True)
+    prob = DeviceProblem(wl, 0, keep_host=True)
+    res = prob.solve(flags=3)
+    res2 = prob.solve(flags=3)
+    assert np.array_equal(res.masks, res2.masks) and np.array_equal(res.decisions, res2.decisions)
+    check_prefix_and_sample(prob, res, 0, wl, prefix_layers=3, n_sample=6,
+                            rng=np.random.default_rng(0))
+    prob.close()
