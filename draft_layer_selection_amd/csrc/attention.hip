@@ -139,26 +139,50 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// MFMA attention partial (bf16, dh = 128): 4 waves x 32 query rows, 64-key tiles.
-//   * the next tile's K/V are loaded into registers while the current tile is computed,
-//     then written to the other LDS buffer: one barrier per tile;
-//   * threads 0..127 stage K rows as they are ([key][dh]); threads 128..255 each load an
-//     8-key x 8-dh block of V, transpose it in registers and store 8-key rows of V^T, so the
-//     P.V MFMA reads its operand with 8-byte LDS loads;
-//   * softmax in the log2 domain on raw scores: p = exp2(s*c - m*c), c = log2(e)/sqrt(dh);
-//     the O rescale is skipped when no lane's running max moved.
+// MFMA attention partial (bf16, dh = 128): 8 waves x 32 query rows = 256 query rows per
+// workgroup (one workgroup per CU), 64-key tiles in a 3-stage LDS ring, so two tiles are in
+// flight while one is computed.
+//   * K and V tiles go global -> LDS with global_load_lds_dwordx4 (1 KB = 4 keys x 256 B per
+//     wave instruction), both kept as [key][dh]; the barrier between tiles is a bare s_barrier
+//     after a per-wave vmcnt wait (a fenced barrier would drain the tiles in flight).
+//   * LDS has 64 banks x 4 B.  K: 16-byte chunk c of key k lives in slot c ^ (k & 15), so the
+//     16-byte reads of 16 consecutive keys are conflict-free.  V: chunk c of key k lives in
+//     slot c ^ (4 * (k & 3)), so the transposing reads below are conflict-free.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query's 32 scores per tile.
+//   * O^T += V^T P^T: the V^T operand is read with ds_read_b64_tr_b16, which hands lane i of
+//     each 16-lane group element (i % 4) of the 8 bytes addressed by lane 4e + i/4 as its
+//     element e; lane (g, e, q) therefore addresses V[key 4*(g/2) + e][dh 16*(g%2) + 4q ..+3]
+//     of the MFMA step and receives V^T[dh][4 consecutive keys] exactly as the MFMA wants.
+//   * softmax in the log2 domain on the hardware v_exp_f32: p = 2^(s*c - m*c),
+//     c = log2(e)/sqrt(dh), with a lazily raised reference m (raised, and O and l rescaled,
+//     only when a score exceeds it by more than 2^8 in p); exact because l carries the same m.
 // ------------------------------------------------------------------------------------
 constexpr int DHM = 128;
-constexpr int KT = 64;            // keys per tile
-constexpr int K_PITCH = DHM + 8;  // LDS row pitch of K [key][dh] (bf16 elements)
-constexpr int V_PITCH = KT + 8;   // LDS row pitch of V^T [dh][key]
+constexpr int KT = 64;              // keys per tile
+constexpr int QB = 256;             // query rows per workgroup
+constexpr int NST = 3;              // LDS ring stages
+constexpr float RESCALE_LOG2 = 8.f; // allowed growth of p above 1 before rescaling
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) unsigned char*)(p));
+}
 
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
+// s_waitcnt with vmcnt = n (n <= 15) and no wait on the other counters (gfx9 encoding)
+__device__ __forceinline__ void attn_wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8)); break;
+    default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+  }
+}
+
+__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int4 wk = a.work[blockIdx.x];
   const AttnSeq S = a.seqs[wk.x];
   const int c = wk.y, qb = wk.z, sp = wk.w;
@@ -166,13 +190,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const int nq = G * S.M;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int t = qb * 128 + wave * 32 + l32;
+  const int t = qb * QB + wave * 32 + l32;
   const bool tvalid = t < nq;
   const int tt = tvalid ? t : nq - 1;
   const int row = S.row_off + tt / G;
   const int h = c * G + tt % G;
   const int k0 = sp * S.chunk;
   const int k1 = min(S.ctx, k0 + S.chunk);
+  const int ntiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
   const float cs = a.scale_log2;
 
   // this lane's query row as the B operand of S^T = K Q^T: 8 K-steps of 16 dh
@@ -181,58 +206,32 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
 
-  __shared__ bf16 Ks[2][KT * K_PITCH];
-  __shared__ bf16 Vt[2][DHM * V_PITCH];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NST][2][KT * 256];
 
-  const bf16* kbase = (const bf16*)S.k + (size_t)c * S.cap * DHM;
-  const bf16* vbase = (const bf16*)S.v + (size_t)c * S.cap * DHM;
-  const bool k_role = tid < 128;
-  const int u = tid & 127;
-  bf16x8 stg[8];
-  bf16x8 zero8;
+  // DMA: per stage 32 chunks (16 of K, 16 of V) of 4 keys; wave w issues chunks w + 8j.
+  // Lane -> key 4*(chunk%16) + lane/16, LDS slot lane%16 <- global 16-byte chunk
+  // slot ^ swz(key), swz = key & 15 for K and 4*(key & 3) for V.
+  const bf16* dsrc[4];
+  int dkey[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zero8[e] = (bf16)0.f;
-
-  auto load_tile = [&](int kt) {
-    if (k_role) {
-      const int key = kt + (u >> 1);
-      const bf16* src = kbase + (size_t)key * DHM + (u & 1) * 64;
+  for (int j = 0; j < 4; ++j) {
+    const int q = wave + 8 * j;  // 0..31
+    const int kk = 4 * (q & 15) + (lane >> 4);
+    const bool isv = q >= 16;
+    const int swz = isv ? 4 * (kk & 3) : (kk & 15);
+    const bf16* base = (const bf16*)(isv ? S.v : S.k) + (size_t)c * S.cap * DHM;
+    dsrc[j] = base + 8 * ((lane & 15) ^ swz);
+    dkey[j] = kk;
+  }
+  auto issue = [&](int tile, int slot) {
+    const int kt = k0 + tile * KT;
+    const bool full = kt + KT <= k1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) stg[e] = key < k1 ? *(const bf16x8*)(src + 8 * e) : zero8;
-    } else {
-      const int kb8 = u & 7, j = u >> 3;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int key = kt + 8 * kb8 + r;
-        stg[r] = key < k1 ? *(const bf16x8*)(vbase + (size_t)key * DHM + 8 * j) : zero8;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if (k_role) {
-      bf16* dst = &Ks[buf][(u >> 1) * K_PITCH + (u & 1) * 64];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) *(bf16x8*)(dst + 8 * e) = stg[e];
-    } else {
-      // stg[r] holds V[key 8*kb8 + r][dh 8j .. 8j+7]; word k of it = dh pair (2k, 2k+1).
-      // Column cc of the block (dh 8j + cc) as 8 keys: word m = (V[2m][cc], V[2m+1][cc]).
-      const int kb8 = u & 7, j = u >> 3;
-      u32x4 w[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) w[r] = as_u32x4(stg[r]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          u32x4 col;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const unsigned lo = w[2 * m][k], hw = w[2 * m + 1][k];
-            col[m] = b == 0 ? ((lo & 0xFFFFu) | (hw << 16)) : ((lo >> 16) | (hw & 0xFFFF0000u));
-          }
-          *(u32x4*)(&Vt[buf][(8 * j + 2 * k + b) * V_PITCH + 8 * kb8]) = col;
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave + 8 * j;
+      const int key = full ? kt + dkey[j] : min(kt + dkey[j], k1 - 1);  // clamped rows masked
+      __builtin_amdgcn_global_load_lds((const void*)(dsrc[j] + (size_t)key * DHM),
+                                       (void*)(&ring[slot][q >> 4][(q & 15) * 1024]), 16, 0, 0);
     }
   };
 
@@ -241,28 +240,53 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
+  float m = -INFINITY, lsum = 0.f;  // m: reference max of raw scores, shared by lanes l, l^32
+  const float thresh = RESCALE_LOG2 / cs;
 
-  int buf = 0;
-  if (k0 < k1) {
-    load_tile(k0);
-    store_tile(0);
+  // Loop-invariant LDS byte offsets within a stage.  K read for K-step ks of key l32 (+32 per
+  // key block): chunk 2ks + hi in slot chunk ^ (key & 15).  V^T read (transposing) of lane
+  // (g = lane/16, e = (lane/4)%4, q = lane%4) for dh block db: key 4*(g/2) + e (+ the key
+  // offset of the MFMA step, a multiple of 8), dh 32db + 16(g%2) + 4q, i.e. chunk
+  // 4db + 2(g%2) + q/2, half q%2, slot chunk ^ 4*(key & 3) = chunk ^ 4e.
+  int koff[8], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = l32 * 256 + 16 * ((2 * ks + hi) ^ (l32 & 15));
+  {
+    const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
+    const int key = 4 * (tg >> 1) + te;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int ch = 4 * db + 2 * (tg & 1) + (tq >> 1);
+      voff[db] = key * 256 + 16 * (ch ^ (4 * te)) + 8 * (tq & 1);
+    }
   }
-  __syncthreads();
-  for (int kt = k0; kt < k1; kt += KT) {
-    const bool more = kt + KT < k1;
-    if (more) load_tile(kt + KT);
+  bf16x2 ones2;
+  ones2[0] = (bf16)1.f;
+  ones2[1] = (bf16)1.f;
+
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < ntiles) issue(p, p);
+
+  for (int it = 0; it < ntiles; ++it) {
+    attn_wait_vmcnt(4 * min(NST - 2, ntiles - 1 - it));  // this wave's part of tile `it`
+    asm volatile("s_barrier" ::: "memory");              // ... and everybody else's
+    if (it + NST - 1 < ntiles) issue(it + NST - 1, (it + NST - 1) % NST);
+    const int kt = k0 + it * KT;
+    const unsigned char* stage = &ring[it % NST][0][0];
 
     // scores: two 32-key blocks; lane holds query l32, keys 8*(r/4) + 4*hi + r%4
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf =
-            *(const bf16x8*)(&Ks[buf][(kb * 32 + l32) * K_PITCH + ks * 16 + hi * 8]);
+    for (int ks = 0; ks < 8; ++ks) {
+      const unsigned char* kp = stage + koff[ks];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *(const bf16x8*)(kp + kb * 32 * 256);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
@@ -281,44 +305,48 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[1][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {  // some running max moved: rescale
-      const float corr = exp2f((m - mn) * cs);
+    if (__builtin_amdgcn_ballot_w64(mt > m + thresh) != 0) {  // some reference too low: raise
+      const float mn = mt > m + thresh ? mt : m;
+      const float corr = __builtin_amdgcn_exp2f((m - mn) * cs);
       lsum *= corr;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+      m = mn;
     }
-    m = mn;
-    const float mc = mn * cs;
+    const float mc = m * cs;
 
+    const unsigned char* vp[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vp[db] = stage + KT * 256 + voff[db];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         bf16x8 pf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(fmaf(sacc[kb][8 * st + e], cs, -mc));
-          lsum += p;
-          pf[e] = (bf16)p;
+        for (int e = 0; e < 8; ++e)
+          pf[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * st + e], cs, -mc));
+        // the denominator sums exactly the rounded p that enter the P.V product
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 pp;
+          pp[0] = pf[e];
+          pp[1] = pf[e + 1];
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, lsum, false);
         }
-        // V^T operand: keys kb*32 + 16*st + 8*(e/4) + 4*hi + e%4 for e = 0..7
-        const int kofs = kb * 32 + 16 * st + 4 * hi;
+        // V^T operand rows dh = 32db + l32, keys kb*32 + 16st + 4hi + (0..3, 8..11)
+        const int kofs = (kb * 32 + 16 * st) * 256;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16* vrow = &Vt[buf][(db * 32 + l32) * V_PITCH + kofs];
-          const bf16x4 lo = *(const bf16x4*)(vrow);
-          const bf16x4 hv = *(const bf16x4*)(vrow + 8);
-          const bf16x8 vf = __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7);
+          const s16x4 lo = lds_read_tr16(vp[db] + kofs);
+          const s16x4 hv = lds_read_tr16(vp[db] + kofs + 8 * 256);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
   }
   lsum += __shfl_xor(lsum, 32, 64);
   if (!tvalid) return;
@@ -364,22 +392,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const float s_self = warp_sum(d) * a.scale_log2;
   const size_t qrow = (size_t)r * a.hq + h;
   const size_t split_stride = (size_t)a.R * a.hq;
-  float mx = s_self;
-  for (int sp = 0; sp < S.nsplit; ++sp) mx = fmaxf(mx, a.Mpart[sp * split_stride + qrow]);
+  // lane sp < nsplit holds split sp's (max, denominator); weights 2^(m_sp - M)
+  const bool has = lane < S.nsplit;
+  const float ms = has ? a.Mpart[lane * split_stride + qrow] : -INFINITY;
+  const float ls = has ? a.Lpart[lane * split_stride + qrow] : 0.f;
+  const float mx = fmaxf(warp_max(ms), s_self);
+  const float wsp = has ? exp2f(ms - mx) : 0.f;
   const float w_self = exp2f(s_self - mx);
-  float den = w_self;
-  for (int sp = 0; sp < S.nsplit; ++sp) {
-    const float ms = a.Mpart[sp * split_stride + qrow];
-    den += exp2f(ms - mx) * a.Lpart[sp * split_stride + qrow];
-  }
+  const float den = warp_sum(wsp * ls) + w_self;
   const float inv = 1.0f / den;
   T* out = (T*)a.O + qrow * a.dh;
   for (int e = lane; e < a.dh; e += 64) {
     float num = w_self * vs[e];
     for (int sp = 0; sp < S.nsplit; ++sp) {
-      const float ms = a.Mpart[sp * split_stride + qrow];
-      const float wsp = exp2f(ms - mx);
-      num = fmaf(wsp, a.Opart[(sp * split_stride + qrow) * a.dh + e], num);
+      const float w = __shfl(wsp, sp, 64);
+      num = fmaf(w, a.Opart[(sp * split_stride + qrow) * a.dh + e], num);
     }
     out[e] = from_f32<T>(num * inv);
   }
@@ -387,7 +414,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 }  // namespace
 
-int attention_qblock(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? 128 : 64; }
+int attention_qblock(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? QB : 64; }
+int attention_target_wgs(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? 256 : 1024; }
 
 hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s) {
   const int waves = a.R * (a.hq + 2 * a.hkv);
@@ -402,7 +430,7 @@ hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
   if (act == ACT_BF16 && a.dh == 128) {
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3(n_work), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_mfma_kernel, dim3(n_work), dim3(512), 0, s, a);
   } else if (act == ACT_BF16) {
     if (a.dh != 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_valu_kernel<bf16, 64>), dim3(n_work), dim3(64), 0, s, a);

@@ -7,8 +7,9 @@
 //     tile = 64*NG columns x 32*MB rows; one workgroup per CU (the LDS ring takes ~128-144 KB);
 //   * weights and activations go global -> LDS with global_load_lds_dwordx4 (no registers),
 //     8 lanes per 128-byte row segment, in a ring of S stages of 64 K each, so S-1 stages are
-//     in flight; 16-byte slots are XOR-swizzled by row so the MFMA-layout reads are
-//     bank-conflict free;
+//     in flight; the 16-byte slot of chunk c in stage row r is c ^ ((r >> 1) & 7): LDS has
+//     64 banks x 4 B and serves 16-byte reads 16 lanes at a time, so 16 consecutive 128-byte
+//     rows must land on 16 distinct (row parity, slot) pairs for conflict-free MFMA reads;
 //   * the barrier between stages is a bare s_barrier: each wave first waits (vmcnt) for its own
 //     loads of the stage, and a fenced barrier would instead drain every load in flight;
 //   * activations are re-read from L2 once per column tile, i.e. R/(64*NG) times the weight
@@ -214,14 +215,14 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
   const bf16* A = (const bf16*)a.A;
 
   // Loader: chunk q = 8 stage rows; lane -> row 8q + lane/8, LDS slot lane%8 which holds the
-  // row's global 16-byte chunk (lane%8) ^ (row%8).
+  // row's global 16-byte chunk (lane%8) ^ ((row >> 1) % 8).
   const bf16* src[PER_WAVE];
   const int rin = lane >> 3;
-  const int cglob = (lane & 7) ^ rin;
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int q = wave + 8 * j;
     const int r = 8 * q + rin;
+    const int cglob = (lane & 7) ^ ((r >> 1) & 7);
     if (q >= NCH) {
       src[j] = W;
     } else if (r < WR) {
@@ -272,12 +273,12 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const int r = 64 * grp + 32 * cb + l32;
-        wf[cb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ (r & 7)));
+        wf[cb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int r = WR + 32 * mb + l32;
-        af[mb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ (r & 7)));
+        af[mb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {

@@ -109,10 +109,20 @@ struct ItemSeq {   // one (item, sequence)
   int pad0, pad1;
 };
 
+// E[r] = state_old[row_state[r]] + sum_s P[s][r]: the item applied to every source row and
+// to the reference row (K splits added in a fixed order, then the residual).
+struct ReduceArgs {
+  const float* P;          // [splits][R][d]
+  int splits, R, d;
+  const float* state_old;  // [S][Bm+1][d]
+  const int* row_state;    // [R] flat index into state_old rows
+  float* E;                // [R][d]
+};
+
 struct SelectArgs {
   int item, n_items, B, Bm, d, mw, n_seqs;
-  const float* P;          // [splits][Rtot][d] partial item outputs (before residual)
-  int splits, Rtot;
+  const float* E;          // [Rtot][d] item outputs incl. residual (ReduceArgs::E)
+  int Rtot;
   const float* state_old;  // [S][Bm+1][d], index Bm = reference
   float* state_new;
   const uint8_t* valid_old;  // [S][Bm]
@@ -148,10 +158,13 @@ hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_init(const InitArgs& a, hipStream_t s);
 
 // rows of Q per attention workgroup for the given activation type / head size
 int attention_qblock(int act, int dh);
+// workgroups the context splits should fill per attention launch
+int attention_target_wgs(int act, int dh);
 
 }  // namespace ks

@@ -57,7 +57,7 @@ struct Carver {
 
 // Byte offsets of the per-solve map / launch tables (same layout on host and device).
 struct MapLayout {
-  size_t exec, next, rowseq, info, work, aseq, rope, x0, init, total, max_work;
+  size_t exec, next, rowseq, rowstate, info, work, aseq, rope, x0, init, total, max_work;
 };
 
 MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int hkv, int G,
@@ -67,6 +67,7 @@ MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int
   L.exec = c.take((size_t)L2 * S * Bm * 4);
   L.next = c.take((size_t)L2 * S * Bm * 4);
   L.rowseq = c.take((size_t)L2 * Rmax * 4);
+  L.rowstate = c.take((size_t)L2 * Rmax * 4);
   L.info = c.take((size_t)L2 * S * sizeof(ks::ItemSeq));
   L.max_work = (size_t)n_layers * S * hkv * ((G * Bm + 63) / 64) * asplit_max;
   L.work = c.take(L.max_work * 16);
@@ -107,6 +108,7 @@ struct knapspec_model {
   void* o = nullptr;
   void* h = nullptr;
   float* P = nullptr;
+  float* E = nullptr;
   float* Opart = nullptr;
   float* Mpart = nullptr;
   float* Lpart = nullptr;
@@ -124,6 +126,12 @@ struct knapspec_model {
   double k_ms[KNAPSPEC_KERNEL_CLASSES] = {};
   int64_t k_count[KNAPSPEC_KERNEL_CLASSES] = {};
 
+  // private stream + captured graph of the last solve configuration
+  hipStream_t own_stream = nullptr;
+  hipEvent_t ev_in = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  std::vector<int64_t> gkey;
+
   // pinned host staging
   char* h_maps = nullptr;
   char* h_out = nullptr;
@@ -131,6 +139,9 @@ struct knapspec_model {
 
   ~knapspec_model() {
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    if (gexec) (void)hipGraphExecDestroy(gexec);
+    if (ev_in) (void)hipEventDestroy(ev_in);
+    if (own_stream) (void)hipStreamDestroy(own_stream);
     if (ws) (void)hipFree(ws);
     if (h_maps) (void)hipHostFree(h_maps);
     if (h_out) (void)hipHostFree(h_out);
@@ -352,6 +363,7 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   const size_t o_o = c.take(R * m->qdim * m->elem);
   const size_t o_h = c.take(R * d.d_ff * m->elem);
   const size_t o_P = c.take(m->p_floats * 4);
+  const size_t o_E = c.take(R * D * 4);
   const size_t o_Op = c.take((size_t)ASPLIT_MAX * R * m->qdim * 4);
   const size_t o_Mp = c.take((size_t)ASPLIT_MAX * R * d.n_q_heads * 4);
   const size_t o_Lp = c.take((size_t)ASPLIT_MAX * R * d.n_q_heads * 4);
@@ -380,6 +392,12 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
     delete m;
     return fail(KNAPSPEC_ENOMEM, "pinned host staging allocation failed");
   }
+  if (hipStreamCreateWithFlags(&m->own_stream, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&m->ev_in, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    delete m;
+    return fail(KNAPSPEC_EHIP, "stream/event creation failed");
+  }
   char* ws = m->ws;
   m->state[0] = (float*)(ws + o_state);
   m->state[1] = m->state[0] + S * (Bm + 1) * D;
@@ -394,6 +412,7 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   m->o = ws + o_o;
   m->h = ws + o_h;
   m->P = (float*)(ws + o_P);
+  m->E = (float*)(ws + o_E);
   m->Opart = (float*)(ws + o_Op);
   m->Mpart = (float*)(ws + o_Mp);
   m->Lpart = (float*)(ws + o_Lp);
@@ -574,7 +593,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
 
   // ---- build the map/launch tables in pinned host memory
   const MapLayout ml = map_layout(L2, d.n_layers, S, Bm, m->Rmax, hkv, G, dh, ASPLIT_MAX);
-  const size_t o_exec = ml.exec, o_next = ml.next, o_rowseq = ml.rowseq, o_info = ml.info,
+  const size_t o_exec = ml.exec, o_next = ml.next, o_rowseq = ml.rowseq,
+               o_rowstate = ml.rowstate, o_info = ml.info,
                o_work = ml.work, o_aseq = ml.aseq, o_rope = ml.rope, o_x0 = ml.x0,
                o_init = ml.init, max_work = ml.max_work;
   const size_t qb_rows = ks::attention_qblock(m->act, dh);
@@ -583,6 +603,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   int32_t* exec_row = (int32_t*)(hm + o_exec);
   int32_t* next_row = (int32_t*)(hm + o_next);
   int32_t* row_seq = (int32_t*)(hm + o_rowseq);
+  int32_t* row_state = (int32_t*)(hm + o_rowstate);
   ks::ItemSeq* info = (ks::ItemSeq*)(hm + o_info);
   int4* work = (int4*)(hm + o_work);
   ks::AttnSeq* aseq = (ks::AttnSeq*)(hm + o_aseq);
@@ -597,7 +618,12 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       const SeqPlan& p = plan[q];
       const int off = row_off[(size_t)i * S + q];
       const int M = (int)p.src[i].size() + 1;
-      for (int r = 0; r < M; ++r) row_seq[(size_t)i * m->Rmax + off + r] = q;
+      for (int r = 0; r < M; ++r) {
+        row_seq[(size_t)i * m->Rmax + off + r] = q;
+        // state row the item is applied to: source budget, or the reference (index Bm)
+        row_state[(size_t)i * m->Rmax + off + r] =
+            q * (Bm + 1) + (r + 1 < M ? p.src[i][r] : Bm);
+      }
       int32_t* er = exec_row + ((size_t)i * S + q) * Bm;
       for (int r = 0; r + 1 < M; ++r) er[p.src[i][r] + p.w[i]] = off + r;
       ks::ItemSeq& in = info[(size_t)i * S + q];
@@ -625,7 +651,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     int base = 0;
     for (int q = 0; q < S; ++q)
       base += hkv * (int)((G * (plan[q].src[i].size() + 1) + qb_rows - 1) / qb_rows);
-    const int target = m->act == ks::ACT_BF16 ? 512 : 1024;
+    const int target = ks::attention_target_wgs(m->act, dh);
     work_off[l] = (int)nw;
     for (int q = 0; q < S; ++q) {
       const knapspec_seq& sq = args->seqs[q];
@@ -669,12 +695,25 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     init_rows[2 * q + 1] = row_off[q] + (int)plan[q].src[0].size();
   }
 
-  hipStream_t st = (hipStream_t)args->hip_stream;
+  // ---- output staging layout (pinned host)
+  char* ho = m->h_out;
+  Carver oc;
+  const size_t ho_masks = oc.take((size_t)S * Bm * mw * 8);
+  const size_t ho_cos = oc.take((size_t)S * Bm * 4);
+  const size_t ho_valid = oc.take((size_t)S * Bm);
+  const size_t ho_dec = oc.take((size_t)S * L2 * Bm);
+  const size_t ho_mar = oc.take((size_t)S * L2 * Bm * 4);
+  const bool want_dec = (args->flags & KNAPSPEC_RETURN_DECISIONS) != 0;
+  const bool want_mar = (args->flags & KNAPSPEC_RETURN_MARGINS) != 0;
+
+  // All device work of one solve, enqueued on `st`: map upload, the DP, result copies.
+  auto enqueue = [&](hipStream_t st) -> int {
   char* dm = m->maps;
   HIPCHK(hipMemcpyAsync(dm, hm, ml.total, hipMemcpyHostToDevice, st));
   const int32_t* d_exec = (const int32_t*)(dm + o_exec);
   const int32_t* d_next = (const int32_t*)(dm + o_next);
   const int32_t* d_rowseq = (const int32_t*)(dm + o_rowseq);
+  const int32_t* d_rowstate = (const int32_t*)(dm + o_rowstate);
   const ks::ItemSeq* d_info = (const ks::ItemSeq*)(dm + o_info);
   const int4* d_work = (const int4*)(dm + o_work);
   const ks::AttnSeq* d_aseq = (const ks::AttnSeq*)(dm + o_aseq);
@@ -700,8 +739,6 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     HIPCHK(ks::launch_init(ia, st));
     prof_end(m, pk, st);
   }
-  const bool want_dec = (args->flags & KNAPSPEC_RETURN_DECISIONS) != 0;
-  const bool want_mar = (args->flags & KNAPSPEC_RETURN_MARGINS) != 0;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
 
   auto gemm = [&](const void* A, int lda, int R, const void* W, int K, int N, int mode,
@@ -805,6 +842,17 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
                 KNAPSPEC_K_GEMM_DOWN);
       if (rc) return rc;
     }
+    ks::ReduceArgs ra{};
+    ra.P = m->P;
+    ra.splits = splits;
+    ra.R = R;
+    ra.d = D;
+    ra.state_old = m->state[cur];
+    ra.row_state = d_rowstate + (size_t)i * m->Rmax;
+    ra.E = m->E;
+    const int pkr = prof_begin(m, KNAPSPEC_K_SELECT, st);
+    HIPCHK(ks::launch_reduce(ra, st));
+    prof_end(m, pkr, st);
     ks::SelectArgs sa{};
     sa.item = i;
     sa.n_items = L2;
@@ -813,8 +861,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     sa.d = D;
     sa.mw = mw;
     sa.n_seqs = S;
-    sa.P = m->P;
-    sa.splits = splits;
+    sa.E = m->E;
     sa.Rtot = R;
     sa.state_old = m->state[cur];
     sa.state_new = m->state[cur ^ 1];
@@ -839,14 +886,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     cur ^= 1;
   }
 
-  // ---- results back to the host (one synchronisation)
-  char* ho = m->h_out;
-  Carver oc;
-  const size_t ho_masks = oc.take((size_t)S * Bm * mw * 8);
-  const size_t ho_cos = oc.take((size_t)S * Bm * 4);
-  const size_t ho_valid = oc.take((size_t)S * Bm);
-  const size_t ho_dec = oc.take((size_t)S * L2 * Bm);
-  const size_t ho_mar = oc.take((size_t)S * L2 * Bm * 4);
+  // ---- results back to the host
   HIPCHK(hipMemcpyAsync(ho + ho_masks, m->masks[cur], (size_t)S * Bm * mw * 8,
                         hipMemcpyDeviceToHost, st));
   HIPCHK(hipMemcpyAsync(ho + ho_cos, m->cos, (size_t)S * Bm * 4, hipMemcpyDeviceToHost, st));
@@ -856,8 +896,60 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   if (want_mar)
     HIPCHK(hipMemcpyAsync(ho + ho_mar, m->margins, (size_t)S * L2 * Bm * 4, hipMemcpyDeviceToHost,
                           st));
-  HIPCHK(hipStreamSynchronize(st));
-  if (m->profiling) prof_collect(m);
+  return KNAPSPEC_OK;
+  };
+
+  // ---- run: replay a captured graph of the whole solve when the launch configuration is the
+  //      one captured last (inputs may differ: pointers and values travel in the map upload),
+  //      otherwise capture it; eager launches when profiling or when KNAPSPEC_GRAPHS=0.
+  hipStream_t caller = (hipStream_t)args->hip_stream;
+  const char* genv = std::getenv("KNAPSPEC_GRAPHS");
+  const bool graphs = !m->profiling && !(genv && genv[0] == '0') && m->own_stream;
+  if (!graphs) {
+    int rc = enqueue(caller);
+    if (rc) return rc;
+    HIPCHK(hipStreamSynchronize(caller));
+    if (m->profiling) prof_collect(m);
+  } else {
+    std::vector<int64_t> key;
+    key.reserve(8 + (size_t)S * (L2 + 1));
+    int32_t tau_bits;
+    std::memcpy(&tau_bits, &args->tau, 4);
+    key.insert(key.end(), {S, B, tau_bits, args->max_skip_weight, args->flags});
+    for (int q = 0; q < S; ++q) {
+      key.push_back(args->seqs[q].ctx_len);
+      for (int i = 0; i < L2; ++i) key.push_back(plan[q].w[i]);
+    }
+    hipStream_t own = m->own_stream;
+    HIPCHK(hipEventRecord(m->ev_in, caller));
+    HIPCHK(hipStreamWaitEvent(own, m->ev_in, 0));
+    if (!(m->gexec && key == m->gkey)) {
+      if (m->gexec) {
+        (void)hipGraphExecDestroy(m->gexec);
+        m->gexec = nullptr;
+      }
+      m->gkey.clear();
+      HIPCHK(hipStreamBeginCapture(own, hipStreamCaptureModeThreadLocal));
+      const int rc = enqueue(own);
+      hipGraph_t graph = nullptr;
+      const hipError_t ec = hipStreamEndCapture(own, &graph);
+      if (rc) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+      }
+      if (ec != hipSuccess || !graph)
+        return fail(KNAPSPEC_EHIP, "graph capture failed: %s", hipGetErrorString(ec));
+      const hipError_t ei = hipGraphInstantiate(&m->gexec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (ei != hipSuccess) {
+        m->gexec = nullptr;
+        return fail(KNAPSPEC_EHIP, "graph instantiation failed: %s", hipGetErrorString(ei));
+      }
+      m->gkey = key;
+    }
+    HIPCHK(hipGraphLaunch(m->gexec, own));
+    HIPCHK(hipStreamSynchronize(own));
+  }
 
   const uint64_t* hmask = (const uint64_t*)(ho + ho_masks);
   const float* hcos = (const float*)(ho + ho_cos);

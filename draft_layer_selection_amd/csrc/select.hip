@@ -1,9 +1,11 @@
 // Per-budget execute/skip select of the KnapSpec DP and the DP's initial state.
 //
-// One workgroup per (sequence, budget b) and one per sequence for the full-model reference.
-// The item's GEMM wrote fp32 K-split partials of F_i(x) - x for each source row; this kernel
-// adds the splits and the residual in a fixed order, forms
-//   c_exec = cos(g[b - w_i] + dF, ref'),   c_skip = cos(g[b], ref'),   ref' = ref + dF_ref,
+// reduce_rows: the item's GEMM wrote fp32 K-split partials of F_i(x) - x for each source row
+// and the reference row; one fully parallel pass adds the splits (fixed order) and the
+// residual, E[r] = x_src(r) + dF(r).
+// select: one workgroup per (sequence, budget b) and one per sequence for the reference; it
+// forms
+//   c_exec = cos(E[row of b - w_i], ref'),   c_skip = cos(g[b], ref'),   ref' = E[ref row],
 // keeps the larger (skip on exact ties, NaN as -inf), applies the tau / skip-cap pruning,
 // carries the layer mask, and writes the kept state together with its RMSNorm'd copy in the
 // activation layout of the next item's GEMM (so the norm is fused into the select).
@@ -18,16 +20,17 @@ namespace {
 
 constexpr int SEL_THREADS = 256;
 
-// value of element e of a GEMM row after adding its K splits (fixed order) and the residual
-__device__ __forceinline__ f32x4 row_value(const float* P, int splits, size_t split_stride,
-                                           size_t row_off, const float* res, int e4) {
-  f32x4 v = *(const f32x4*)(P + row_off + 4 * e4);
-  for (int s = 1; s < splits; ++s) {
-    const f32x4 p = *(const f32x4*)(P + s * split_stride + row_off + 4 * e4);
-    v += p;
-  }
-  const f32x4 r = *(const f32x4*)(res + 4 * e4);
-  return r + v;
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  const int d4 = a.d / 4;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)a.R * d4) return;
+  const int r = (int)(idx / d4), e4 = (int)(idx % d4);
+  const size_t split_stride = (size_t)a.R * a.d;
+  const size_t off = (size_t)r * a.d + 4 * e4;
+  f32x4 v = *(const f32x4*)(a.P + off);
+  for (int s = 1; s < a.splits; ++s) v += *(const f32x4*)(a.P + s * split_stride + off);
+  const f32x4 res = *(const f32x4*)(a.state_old + (size_t)a.row_state[r] * a.d + 4 * e4);
+  *(f32x4*)(a.E + off) = res + v;
 }
 
 template <int N>
@@ -71,15 +74,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   const size_t sstride = (size_t)(a.Bm + 1) * a.d;  // per-sequence state stride
   const float* st_old = a.state_old + q * sstride;
   float* st_new = a.state_new + q * sstride;
-  const size_t split_stride = (size_t)a.Rtot * a.d;
-  const size_t ref_poff = (size_t)inf.ref_row * a.d;
-  const float* ref_res = st_old + (size_t)a.Bm * a.d;
+  const float* ref = a.E + (size_t)inf.ref_row * a.d;
   __shared__ float scratch[8 * (SEL_THREADS / 64)];
 
   if (is_ref) {
     float ss[1] = {0.f};
     for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
-      const f32x4 r = row_value(a.P, a.splits, split_stride, ref_poff, ref_res, e4);
+      const f32x4 r = *(const f32x4*)(ref + 4 * e4);
       *(f32x4*)(st_new + (size_t)a.Bm * a.d + 4 * e4) = r;
       ss[0] += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
     }
@@ -98,18 +99,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   const int src = b - inf.w;
   const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
   const bool has_skip = a.valid_old[qb] != 0;
-  const size_t epoff = has_exec ? (size_t)erow * a.d : 0;
-  const float* e_res = st_old + (size_t)(has_exec ? src : 0) * a.d;
+  const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;
   const float* g_row = st_old + (size_t)b * a.d;
 
   // pass 1: rr, er, ee, gr, gg
   float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
   if (has_exec || has_skip) {
     for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
-      const f32x4 r = row_value(a.P, a.splits, split_stride, ref_poff, ref_res, e4);
+      const f32x4 r = *(const f32x4*)(ref + 4 * e4);
       acc[0] += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
       if (has_exec) {
-        const f32x4 ev = row_value(a.P, a.splits, split_stride, epoff, e_res, e4);
+        const f32x4 ev = *(const f32x4*)(e_row + 4 * e4);
         acc[1] += ev[0] * r[0] + ev[1] * r[1] + ev[2] * r[2] + ev[3] * r[3];
         acc[2] += ev[0] * ev[0] + ev[1] * ev[1] + ev[2] * ev[2] + ev[3] * ev[3];
       }
@@ -168,8 +168,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   const float scale = 1.0f / sqrtf(ms + a.eps);
   float* out = st_new + (size_t)b * a.d;
   for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
-    const f32x4 x = take ? row_value(a.P, a.splits, split_stride, epoff, e_res, e4)
-                         : *(const f32x4*)(g_row + 4 * e4);
+    const f32x4 x = take ? *(const f32x4*)(e_row + 4 * e4) : *(const f32x4*)(g_row + 4 * e4);
     *(f32x4*)(out + 4 * e4) = x;
     if (nrow >= 0) store_act<T>(a.xa_next, nrow, a.d, e4, x, scale);
   }
@@ -205,6 +204,12 @@ __global__ __launch_bounds__(SEL_THREADS) void init_kernel(InitArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  const size_t n = (size_t)a.R * (a.d / 4);
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   const dim3 grid(a.n_seqs * (a.B + 1)), block(SEL_THREADS);
