@@ -107,6 +107,16 @@ def algorithmic_work(wl, w_per_seq, ctxs):
                  "mean_rows": sum(sum(pr[0]) for pr in per_item_rows) / L2}
 
 
+def ko_weights(wl, ctx):
+    """Integer item weights at context ctx (same rounding rule as the library; the library's
+    own values are checked against the oracle by the tests)."""
+    lat, s = wl.latency, wl.shape
+    t = [lat.attn_base + lat.attn_per_token * ctx if i % 2 == 0 else lat.mlp
+         for i in range(2 * s.n_layers)]
+    delta = sum(t) / (wl.n_budgets - 1)
+    return [max(1, int(round(x / delta))) for x in t]
+
+
 def cpu_baseline(wl, prob, sample_layers, log_fn):
     """The oracle, untuned, on a bounded prefix of the same solve: the first
     ``sample_layers`` layers (2 items each) of the DP over the same inputs.  The rate is scaled
@@ -172,19 +182,31 @@ def main():
     log(f"[bench] generating and uploading {wl.name} inputs ...")
     prob = DeviceProblem(wl, args.seed, keep_host=want_cpu)
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; warmup {args.warmup}")
+    # one step = one solve; for a multi-sequence preset one step is its whole re-solve
+    # schedule (every sequence re-solved `resolves` times as its context grows)
+    multi = prob.n_resolves > 1
+    solves_per_step = len(prob.ctxs) * prob.n_resolves
+
+    def step(res):
+        if not multi:
+            return prob.solve(result=res)
+        for r in range(prob.n_resolves):
+            res = prob.solve(resolve=r)
+        return res
+
     res = None
     for _ in range(args.warmup):
-        res = prob.solve(result=res)
+        res = step(res)
     torch.cuda.synchronize()
 
-    # timed region: K full solves back to back (the headline number)
+    # timed region: K steps back to back (the headline number)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        res = prob.solve(result=res)
+        res = step(res)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    log(f"[bench] {args.steps} solves in {elapsed:.3f}s")
+    log(f"[bench] {args.steps} steps ({args.steps * solves_per_step} solves) in {elapsed:.3f}s")
 
     # roofline region: the same K solves again with every kernel launch bracketed by HIP
     # events on the solve stream (per-kernel-class durations; adds event records per launch)
@@ -192,18 +214,30 @@ def main():
     torch.cuda.synchronize()
     t_prof = time.perf_counter()
     for _ in range(args.steps):
-        res = prob.solve(result=res)
+        res = step(res)
     torch.cuda.synchronize()
     elapsed_prof = time.perf_counter() - t_prof
     ktimes = prob.model.kernel_times()
     prob.model.set_profiling(False)
     log(f"[bench] profiled pass: {args.steps} solves in {elapsed_prof:.3f}s")
 
-    solves_per_s = args.steps / elapsed
+    solves_per_s = args.steps * solves_per_step / elapsed
     ms_per_step = 1000.0 * elapsed / args.steps
-    w_per_seq = [res.item_weight[q] for q in range(len(prob.ctxs))]
-    cls, tot = algorithmic_work(wl, w_per_seq, prob.ctxs)
-    achieved_gbs = tot["total_bytes"] * solves_per_s / 1e9
+    # algorithmic work of one step (summed over the schedule's solves)
+    cls, tot = None, None
+    for r in range(prob.n_resolves):
+        ctxs = prob.resolve_ctxs(r) if multi else prob.ctxs
+        w_per_seq = [ko_weights(wl, c) for c in ctxs]
+        c_r, t_r = algorithmic_work(wl, w_per_seq, ctxs)
+        if cls is None:
+            cls, tot = c_r, t_r
+        else:
+            for k in cls:
+                for f in ("bytes", "flops", "launches"):
+                    cls[k][f] += c_r[k][f]
+            for f in ("weight_bytes", "kv_bytes", "state_bytes", "total_bytes", "total_flops"):
+                tot[f] += t_r[f]
+    achieved_gbs = tot["total_bytes"] * args.steps / elapsed / 1e9
 
     # dominant kernel class by measured time
     per_class = {}
@@ -252,16 +286,17 @@ def main():
         "vs_baseline": None,
         "dtype": wl.shape.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": wl.shape.n_layers, "d_model": wl.shape.d_model,
+        "config": {"workload": wl.name, "resolves": prob.n_resolves, "layers": wl.shape.n_layers, "d_model": wl.shape.d_model,
                    "heads_q_kv": [wl.shape.n_q_heads, wl.shape.n_kv_heads],
                    "head_dim": wl.shape.head_dim, "d_ff": wl.shape.d_ff, "ctx": prob.ctxs,
                    "budgets": wl.n_budgets, "gamma": list(wl.gamma), "n_seqs": len(prob.ctxs),
                    "parallelism": "single-gpu"},
         "achieved_hbm_gbs": round(achieved_gbs, 1),
         "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-        "algorithmic_bytes_per_solve": int(tot["total_bytes"]),
-        "algorithmic_flops_per_solve": float(tot["total_flops"]),
-        "mfma_frac": round(tot["total_flops"] * solves_per_s / 1e12 /
+        "algorithmic_bytes_per_step": int(tot["total_bytes"]),
+        "algorithmic_flops_per_step": float(tot["total_flops"]),
+        "solves_per_step": solves_per_step,
+        "mfma_frac": round(tot["total_flops"] * args.steps / elapsed / 1e12 /
                            MFMA_PEAK_TFLOPS[wl.shape.dtype], 4),
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -269,6 +304,8 @@ def main():
         "kernel_ms_per_solve": round(tot_ms / args.steps, 4),
         "ms_per_step_profiled": round(1000.0 * elapsed_prof / args.steps, 4),
         "best": {"budget": int(res.best_budget[0]), "gamma": int(res.best_gamma[0])},
+        "note": ("multi-sequence preset: one step = every sequence re-solved on its schedule; "
+                 "value counts single-sequence solves") if multi else None,
     }
     print(json.dumps(line), flush=True)
     prob.close()

@@ -130,7 +130,8 @@ struct knapspec_model {
   hipStream_t own_stream = nullptr;
   hipEvent_t ev_in = nullptr;
   hipGraphExec_t gexec = nullptr;
-  std::vector<int64_t> gkey;
+  std::vector<int64_t> gkey;      // configuration of the captured graph
+  std::vector<int64_t> last_key;  // configuration of the previous solve
 
   // pinned host staging
   char* h_maps = nullptr;
@@ -900,8 +901,9 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   };
 
   // ---- run: replay a captured graph of the whole solve when the launch configuration is the
-  //      one captured last (inputs may differ: pointers and values travel in the map upload),
-  //      otherwise capture it; eager launches when profiling or when KNAPSPEC_GRAPHS=0.
+  //      one captured last (inputs may differ: pointers and values travel in the map upload);
+  //      capture a configuration the second time in a row it is seen; otherwise launch eagerly
+  //      (always when profiling or when KNAPSPEC_GRAPHS=0).
   hipStream_t caller = (hipStream_t)args->hip_stream;
   const char* genv = std::getenv("KNAPSPEC_GRAPHS");
   const bool graphs = !m->profiling && !(genv && genv[0] == '0') && m->own_stream;
@@ -923,7 +925,13 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     hipStream_t own = m->own_stream;
     HIPCHK(hipEventRecord(m->ev_in, caller));
     HIPCHK(hipStreamWaitEvent(own, m->ev_in, 0));
-    if (!(m->gexec && key == m->gkey)) {
+    const bool replay = m->gexec && key == m->gkey;
+    const bool capture = !replay && key == m->last_key;  // capture once a configuration repeats
+    m->last_key = key;
+    if (!replay && !capture) {
+      int rc = enqueue(own);
+      if (rc) return rc;
+    } else if (capture) {
       if (m->gexec) {
         (void)hipGraphExecDestroy(m->gexec);
         m->gexec = nullptr;
@@ -947,7 +955,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       }
       m->gkey = key;
     }
-    HIPCHK(hipGraphLaunch(m->gexec, own));
+    if (replay || capture) HIPCHK(hipGraphLaunch(m->gexec, own));
     HIPCHK(hipStreamSynchronize(own));
   }
 

@@ -61,25 +61,27 @@ def check_structure(res, q, t, B, gamma, n_items, t_target):
     assert (pick[0], pick[1]) == (int(res.best_budget[q]), int(res.best_gamma[q]))
 
 
-def check_prefix_and_sample(prob, res, q, wl, prefix_layers, n_sample, rng):
+def check_prefix_and_sample(prob, res, q, wl, prefix_layers, n_sample, rng, ctx=None, x0=None):
     s = wl.shape
     n_items = 2 * s.n_layers
     beta = BETA[s.dtype]
     lat = wl.latency
-    t = ko.item_latencies(s.n_layers, prob.ctxs[q], lat.attn_base, lat.attn_per_token, lat.mlp)
+    ctx = prob.ctxs[q] if ctx is None else ctx
+    x0 = prob.host_x0[q] if x0 is None else x0
+    t = ko.item_latencies(s.n_layers, ctx, lat.attn_base, lat.attn_per_token, lat.mlp)
     w = ko.item_weights(t, wl.n_budgets)
     assert np.array_equal(res.item_weight[q], w.astype(np.int32))
     check_structure(res, q, t, wl.n_budgets, wl.gamma, n_items, float(np.sum(t)))
-    items = ko.DecoderItems(decoder_shape(wl), prob.host_layers, prob.host_kv[q], prob.ctxs[q])
+    items = ko.DecoderItems(decoder_shape(wl), prob.host_layers, prob.host_kv[q], ctx)
     # oracle on the first items: decisions on clean cells must agree
     k = 2 * prefix_layers
     t0 = time.time()
-    pre = ko.knapsack_dp(items, k, w[:k], prob.host_x0[q], wl.n_budgets)
+    pre = ko.knapsack_dp(items, k, w[:k], x0, wl.n_budgets)
     fake = ko.SolveResult(dp=pre, t=t[:k], w=w[:k], masks=None, t_draft=None, t_target=0,
                           best_budget=-1, best_gamma=-1, best_tpt=0)
     clean = clean_cells(fake, beta)
     mism = int(np.sum((res.decisions[q][:k] != pre.decisions) & clean))
-    print(f"  seq {q}: prefix {k} items in {time.time() - t0:.1f}s, clean {clean.sum()}/"
+    print(f"  seq {q} ctx {ctx}: prefix {k} items in {time.time() - t0:.1f}s, clean {clean.sum()}/"
           f"{clean.size}, clean mismatches {mism}", flush=True)
     assert mism == 0
     # oracle forward of sampled returned masks
@@ -91,7 +93,7 @@ def check_prefix_and_sample(prob, res, q, wl, prefix_layers, n_sample, rng):
     picks = sorted(picks)
     bits = ko.unpack_masks(res.masks[q], n_items)[picks]
     t0 = time.time()
-    ev = ko.eval_subsets(items, n_items, prob.host_x0[q], bits)
+    ev = ko.eval_subsets(items, n_items, x0, bits)
     err = np.abs(ev - res.cos[q][picks].astype(np.float64))
     print(f"  seq {q}: P2 on budgets {picks}: max err {err.max():.2e} ({time.time() - t0:.1f}s)",
           flush=True)
@@ -110,4 +112,37 @@ def test_llama3_8b_32k_full():
     assert np.array_equal(res.masks, res2.masks) and np.array_equal(res.decisions, res2.decisions)
     check_prefix_and_sample(prob, res, 0, wl, prefix_layers=3, n_sample=6,
                             rng=np.random.default_rng(0))
+    prob.close()
+
+
+@pytest.mark.timeout(1100)
+def test_llama3_8b_x16_resolve_schedule():
+    """16 sequences, contexts lognormal in [2K, 32K], re-solved every 256 tokens (8 times),
+    all sequences batched into each solve.  Every sequence of every re-solve is checked for
+    the structural properties; two sequences at the first and last re-solve against the
+    oracle (DP prefix and sampled masks)."""
+    from workloads.device import DeviceProblem
+
+    wl = WORKLOADS["llama3_8b_x16"]
+    print(f"\n[case] {wl.name}", flush=True)
+    prob = DeviceProblem(wl, 0, keep_host=True)
+    print(f"  contexts {prob.ctxs}", flush=True)
+    s = wl.shape
+    n_items = 2 * s.n_layers
+    lat = wl.latency
+    rng = np.random.default_rng(1)
+    for r in range(wl.resolves):
+        res = prob.solve(flags=3, resolve=r)
+        ctxs = prob.resolve_ctxs(r)
+        for q in range(len(ctxs)):
+            t = ko.item_latencies(s.n_layers, ctxs[q], lat.attn_base, lat.attn_per_token, lat.mlp)
+            w = ko.item_weights(t, wl.n_budgets)
+            assert np.array_equal(res.item_weight[q], w.astype(np.int32))
+            check_structure(res, q, t, wl.n_budgets, wl.gamma, n_items, float(np.sum(t)))
+        if r in (0, wl.resolves - 1):
+            for q in (int(np.argmin(ctxs)), int(np.argmax(ctxs))):
+                check_prefix_and_sample(prob, res, q, wl, prefix_layers=2, n_sample=3, rng=rng,
+                                        ctx=ctxs[q], x0=prob.resolve_x0[q][r])
+        print(f"  resolve {r}: picks {[(int(b), int(g)) for b, g in zip(res.best_budget, res.best_gamma)]}",
+              flush=True)
     prob.close()

@@ -40,6 +40,7 @@ def test_graph_replays_match_eager():
     wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=3, d_model=1024, d_ff=2048, name="graph_t")
     prob = DeviceProblem(wl, 3, ctxs=[700], caps=[1200], max_budgets=64)
     B = 64
+    prob.model.solve(prob.seq_args(), B, wl.gamma, flags=3)  # first sight: eager; next: capture
     for rep in range(4):
         # new input values in the same buffers: x0 and the first layer's cache
         prob.set_x0(0, synth.x0(wl, 0, rep + 1, seed=3))
@@ -55,6 +56,7 @@ def test_graph_replays_match_eager():
         print(f"replay {rep}: best=({int(g.best_budget[0])}, {int(g.best_gamma[0])}) ok")
     # a different context length changes the launch configuration (recapture), then back
     g2 = prob.model.solve(prob.seq_args([1100]), B, wl.gamma, flags=3)
+    g2 = prob.model.solve(prob.seq_args([1100]), B, wl.gamma, flags=3)
     os.environ["KNAPSPEC_GRAPHS"] = "0"
     try:
         e2 = prob.model.solve(prob.seq_args([1100]), B, wl.gamma, flags=3)
@@ -62,6 +64,7 @@ def test_graph_replays_match_eager():
     finally:
         os.environ.pop("KNAPSPEC_GRAPHS", None)
     _same(g2, e2)
-    g3 = prob.model.solve(prob.seq_args(), B, wl.gamma, flags=3)
-    _same(g3, e3)
+    for _ in range(3):  # eager (new after 1100), capture, replay
+        g3 = prob.model.solve(prob.seq_args(), B, wl.gamma, flags=3)
+        _same(g3, e3)
     prob.close()

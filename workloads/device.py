@@ -57,6 +57,13 @@ class DeviceProblem:
                     self.host_kv[q].append((k, v))
         self.host_x0 = [synth.x0(wl, q, 0, seed) for q in range(len(self.ctxs))]
         self.x0 = [torch.from_numpy(x).to("cuda") for x in self.host_x0]
+        # inputs of the re-solve schedule (multi-sequence presets): x0 of every (seq, resolve),
+        # resident on the device up front
+        self.n_resolves = wl.resolves if wl.n_seqs > 1 else 1
+        self.resolve_x0 = [[synth.x0(wl, q, r, seed) for r in range(self.n_resolves)]
+                           for q in range(len(self.ctxs))]
+        self.resolve_x0_dev = [[torch.from_numpy(x).to("cuda") for x in row]
+                               for row in self.resolve_x0]
         desc = dict(n_layers=s.n_layers, d_model=s.d_model, n_q_heads=s.n_q_heads,
                     n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, d_ff=s.d_ff,
                     dtype=ks.KNAPSPEC_BF16 if s.dtype == "bf16" else ks.KNAPSPEC_F32,
@@ -72,15 +79,24 @@ class DeviceProblem:
         self.host_x0[q] = x
         self.x0[q].copy_(self.torch.from_numpy(x))
 
-    def seq_args(self, ctxs: Optional[List[int]] = None):
+    def seq_args(self, ctxs: Optional[List[int]] = None, resolve: Optional[int] = None):
+        """Arguments of one solve.  With ``resolve`` = r the sequences are at their r-th
+        re-solve: context ctx0 + r * tokens_per_resolve and that re-solve's x0."""
+        if resolve is not None:
+            ctxs = self.resolve_ctxs(resolve)
         ctxs = ctxs if ctxs is not None else self.ctxs
+        x0 = ([self.resolve_x0_dev[q][resolve] for q in range(len(ctxs))] if resolve is not None
+              else self.x0)
         return [{"ctx": ctxs[q], "k_cache": self.k_cache[q], "v_cache": self.v_cache[q],
-                 "x0": self.x0[q]} for q in range(len(ctxs))]
+                 "x0": x0[q]} for q in range(len(ctxs))]
+
+    def resolve_ctxs(self, r: int) -> List[int]:
+        return [c + r * self.wl.tokens_per_resolve for c in self.ctxs]
 
     def solve(self, n_budgets=None, gamma=None, tau=-math.inf, max_skip_weight=-1, flags=0,
-              ctxs=None, result=None):
+              ctxs=None, result=None, resolve=None):
         wl = self.wl
-        return self.model.solve(self.seq_args(ctxs), n_budgets or wl.n_budgets,
+        return self.model.solve(self.seq_args(ctxs, resolve), n_budgets or wl.n_budgets,
                                 gamma or wl.gamma, tau, max_skip_weight, flags, result=result)
 
     def close(self):
