@@ -107,6 +107,106 @@ def algorithmic_work(wl, w_per_seq, ctxs):
                  "mean_rows": sum(sum(pr[0]) for pr in per_item_rows) / L2}
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "draft_layer_selection_amd", "csrc")
+
+
+def kernel_source_sha() -> str:
+    """Hash of the HIP/C++ sources: counter figures taken on other sources are stale."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(nbytes: int):
+    """A plain device copy of known size (torch's copy kernel), for scaling the FETCH_SIZE /
+    WRITE_SIZE counters to bytes."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4}))
+
+
+def _pmc_per_kernel(path_dir, counter):
+    """{kernel name: [per-dispatch counter values]} from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+
+    out = {}
+    for f in glob.glob(os.path.join(path_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            out.setdefault(key, 0.0)
+            out[key] += float(r["Counter_Value"])
+    per = {}
+    for (name, _), v in out.items():
+        per.setdefault(name, []).append(v)
+    return per
+
+
+def summarize_profiles(args):
+    """Write profiles/<kernel>_<workload>.md and profiles/traffic_<workload>.json from a
+    kernel-trace --stats csv and four --pmc runs (bench FETCH_SIZE / WRITE_SIZE, copy
+    FETCH_SIZE / WRITE_SIZE)."""
+    import csv
+
+    stats = list(csv.DictReader(open(args.stats)))
+    fetch = _pmc_per_kernel(args.fetch, "FETCH_SIZE")
+    write = _pmc_per_kernel(args.write, "WRITE_SIZE")
+    cfetch = _pmc_per_kernel(args.copy_fetch, "FETCH_SIZE")
+    cwrite = _pmc_per_kernel(args.copy_write, "WRITE_SIZE")
+    copy_bytes = args.copy_bytes
+
+    def copy_factor(per):
+        # largest dispatch of the copy run is the calibration copy
+        vals = max((v for vs in per.values() for v in vs), default=0.0)
+        return copy_bytes / (vals * 1024.0) if vals else None
+
+    f_fac, w_fac = copy_factor(cfetch), copy_factor(cwrite)
+    rows = []
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        fv, wv = fetch.get(name, []), write.get(name, [])
+        fb = (sum(fv) / len(fv)) * 1024.0 * f_fac if fv and f_fac else None
+        wb = (sum(wv) / len(wv)) * 1024.0 * w_fac if wv and w_fac else None
+        rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["Percentage"]), fb, wb))
+    sha = kernel_source_sha()
+    os.makedirs(PROFILES, exist_ok=True)
+    md = [f"# rocprofv3 summary: {args.workload}", "",
+          f"kernel sources sha256[:16] = {sha}", "",
+          "Commands (run from the repository root on one MI355X; TMPDIR=/tmp):", "```"]
+    md += args.commands.split(";;")
+    md += ["```", "",
+           f"Counter scale: a plain copy of {copy_bytes} bytes reads FETCH_SIZE -> factor "
+           f"{f_fac:.4f} and WRITE_SIZE -> factor {w_fac:.4f} bytes per counted byte (KiB x 1024).",
+           "", "| kernel | calls | avg us | % time | HBM fetch MB/launch | HBM write MB/launch |",
+           "|---|---|---|---|---|---|"]
+    for name, calls, us, pct, fb, wb in rows[:16]:
+        fbs = f"{fb / 1e6:.2f}" if fb is not None else "-"
+        wbs = f"{wb / 1e6:.2f}" if wb is not None else "-"
+        md.append(f"| `{name[:90]}` | {calls} | {us:.1f} | {pct:.1f} | {fbs} | {wbs} |")
+    dom = rows[0]
+    tag = "attention" if "attn" in dom[0] else dom[0].split("(")[0].split()[-1]
+    out_md = os.path.join(PROFILES, f"{tag}_{args.workload}.md")
+    open(out_md, "w").write("\n".join(md) + "\n")
+    traffic = {"workload": args.workload, "kernel": dom[0], "source_sha": sha,
+               "fetch_bytes_per_launch": dom[4], "write_bytes_per_launch": dom[5],
+               "copy_factor_fetch": f_fac, "copy_factor_write": w_fac}
+    json.dump(traffic, open(os.path.join(PROFILES, f"traffic_{args.workload}.json"), "w"), indent=1)
+    print(out_md)
+
+
 def ko_weights(wl, ctx):
     """Integer item weights at context ctx (same rounding rule as the library; the library's
     own values are checked against the oracle by the tests)."""
@@ -163,7 +263,22 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--summarize-profiles", action="store_true")
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--commands", default="")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KnapSpec DP solve runs on a single MI355X "
               "(multi-GPU sharding is a design note, not part of this build); use --gpus 1.",
@@ -260,6 +375,14 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
+    tpath = os.path.join(PROFILES, f"traffic_{wl.name}.json")
+    if os.path.exists(tpath):
+        tr = json.load(open(tpath))
+        kname = "attn_mfma" if dom == "attention" else dom
+        if (tr.get("source_sha") == kernel_source_sha() and kname in tr.get("kernel", "")
+                and tr.get("fetch_bytes_per_launch") is not None):
+            roof["traffic"] = int(tr["fetch_bytes_per_launch"] + (tr["write_bytes_per_launch"] or 0))
+            roof["traffic_algorithmic"] = int(bytes_per_launch)
     roof["kernel"] = dom
     log("[bench] kernel classes (avg us/launch, share of solve):")
     tot_ms = sum(v["total_ms"] for v in per_class.values())
