@@ -12,6 +12,8 @@
 //   combine      : merges the context splits (log-sum-exp) with the row's own position.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -70,6 +72,7 @@ constexpr int VTILE = 32;
 template <class T, int DH>
 __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
   const int4 wk = a.work[blockIdx.x];
+  if (wk.x < 0) return;
   const AttnSeq S = a.seqs[wk.x];
   const int c = wk.y, qb = wk.z, sp = wk.w;
   const int G = a.hq / a.hkv;
@@ -129,8 +132,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
     __syncthreads();
   }
   if (!tvalid) return;
-  const size_t qrow = (size_t)row * a.hq + h;
-  const size_t slot = (size_t)sp * a.Rtot * a.hq + qrow;
+  const size_t slot = attn_slot(S, sp, tt / G, a.hq, h);
   float* o = a.Opart + slot * DH;
 #pragma unroll
   for (int e = 0; e < DH; ++e) o[e] = acc[e];
@@ -140,11 +142,11 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------------------------
 // MFMA attention partial (bf16, dh = 128): 8 waves x 32 query rows = 256 query rows per
-// workgroup (one workgroup per CU), 64-key tiles in a 3-stage LDS ring, so two tiles are in
-// flight while one is computed.
+// workgroup (one workgroup per CU), 64-key tiles.
 //   * K and V tiles go global -> LDS with global_load_lds_dwordx4 (1 KB = 4 keys x 256 B per
-//     wave instruction), both kept as [key][dh]; the barrier between tiles is a bare s_barrier
-//     after a per-wave vmcnt wait (a fenced barrier would drain the tiles in flight).
+//     wave instruction) into a K ring and a V ring of four slots each, both kept as
+//     [key][dh]; the barrier between tiles is a bare s_barrier after a per-wave vmcnt wait (a
+//     fenced barrier would drain the tiles in flight).
 //   * LDS has 64 banks x 4 B.  K: 16-byte chunk c of key k lives in slot c ^ (k & 15), so the
 //     16-byte reads of 16 consecutive keys are conflict-free.  V: chunk c of key k lives in
 //     slot c ^ (4 * (k & 3)), so the transposing reads below are conflict-free.
@@ -156,34 +158,57 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 //   * softmax in the log2 domain on the hardware v_exp_f32: p = 2^(s*c - m*c),
 //     c = log2(e)/sqrt(dh), with a lazily raised reference m (raised, and O and l rescaled,
 //     only when a score exceeds it by more than 2^8 in p); exact because l carries the same m.
+//   * Software pipeline: iteration t issues the score MFMAs of tile t+1 between the
+//     exponentials and P.V MFMAs of tile t, so one wave keeps the matrix core and the vector
+//     ALU busy at once.  K of tile t is read in iteration t-1 and V in iteration t, so
+//     K(t+3) and V(t+2) are fetched in iteration t, two iterations ahead of use.
 // ------------------------------------------------------------------------------------
 constexpr int DHM = 128;
-constexpr int KT = 64;              // keys per tile
-constexpr int QB = 256;             // query rows per workgroup
-constexpr int NST = 3;              // LDS ring stages
-constexpr float RESCALE_LOG2 = 8.f; // allowed growth of p above 1 before rescaling
+constexpr int KT = 64;                 // keys per tile
+constexpr int QB = 256;                // query rows per workgroup
+constexpr int NR = 4;                  // slots of the K ring and of the V ring
+constexpr int TILE_BYTES = KT * DHM * 2;
+constexpr float RESCALE_LOG2 = 8.f;    // allowed growth of p above 1 before rescaling
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(__attribute__((address_space(3))) unsigned char*)(p));
+// transposing LDS read at an LDS-space byte address (kept in LDS space so the constant part
+// of the address folds into the instruction's offset field)
+__device__ __forceinline__ s16x4 lds_read_tr16(const lds_u8* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
-// s_waitcnt with vmcnt = n (n <= 15) and no wait on the other counters (gfx9 encoding)
+// max / sum of a value over the lane pair (l, l ^ 32) with one v_permlane32_swap
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// s_waitcnt with vmcnt = n (even n <= 14; anything else waits for all) and no wait on the
+// other counters (gfx9 encoding: vmcnt low bits [3:0], expcnt [6:4], lgkmcnt [11:8])
 __device__ __forceinline__ void attn_wait_vmcnt(int n) {
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(14 | (7 << 4) | (15 << 8)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8)); break;
     case 8: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8)); break;
     default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
   }
 }
 
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int4 wk = a.work[blockIdx.x];
+  if (wk.x < 0) return;
   const AttnSeq S = a.seqs[wk.x];
   const int c = wk.y, qb = wk.z, sp = wk.w;
   const int G = a.hq / a.hkv;
@@ -192,6 +217,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int t = qb * QB + wave * 32 + l32;
   const bool tvalid = t < nq;
+  // a wave whose 32 query rows are all past the end only helps stage the tiles
+  const bool wactive = qb * QB + wave * 32 < nq;
   const int tt = tvalid ? t : nq - 1;
   const int row = S.row_off + tt / G;
   const int h = c * G + tt % G;
@@ -206,33 +233,46 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
 
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[NST][2][KT * 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char kring[NR][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vring[NR][TILE_BYTES];
 
-  // DMA: per stage 32 chunks (16 of K, 16 of V) of 4 keys; wave w issues chunks w + 8j.
-  // Lane -> key 4*(chunk%16) + lane/16, LDS slot lane%16 <- global 16-byte chunk
-  // slot ^ swz(key), swz = key & 15 for K and 4*(key & 3) for V.
-  const bf16* dsrc[4];
-  int dkey[4];
+  // DMA: a tile is 16 chunks of 4 keys of K and 16 of V; wave w issues chunks w and w + 8 of
+  // each.  Lane -> key 4*chunk + lane/16 of the tile, LDS slot lane%16 <- global 16-byte
+  // chunk slot ^ swz(key), swz = key & 15 for K and 4*(key & 3) for V.  The loads are
+  // range-checked buffer loads whose resource starts at the tile's first key and ends at the
+  // sequence's last cached key: keys past the cache read as zeros (their scores are masked),
+  // and the per-lane byte offsets stay the same for every tile.
+  int kvo[2], vvo[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = wave + 8 * j;  // 0..31
-    const int kk = 4 * (q & 15) + (lane >> 4);
-    const bool isv = q >= 16;
-    const int swz = isv ? 4 * (kk & 3) : (kk & 15);
-    const bf16* base = (const bf16*)(isv ? S.v : S.k) + (size_t)c * S.cap * DHM;
-    dsrc[j] = base + 8 * ((lane & 15) ^ swz);
-    dkey[j] = kk;
+  for (int j = 0; j < 2; ++j) {
+    const int kk = 4 * (wave + 8 * j) + (lane >> 4);
+    kvo[j] = kk * 256 + 16 * ((lane & 15) ^ (kk & 15));
+    vvo[j] = kk * 256 + 16 * ((lane & 15) ^ (4 * (kk & 3)));
   }
-  auto issue = [&](int tile, int slot) {
-    const int kt = k0 + tile * KT;
-    const bool full = kt + KT <= k1;
+  const char* khead = (const char*)S.k + (size_t)c * S.cap * DHM * 2;
+  const char* vhead = (const char*)S.v + (size_t)c * S.cap * DHM * 2;
+  auto tile_rsrc = [&](const char* head, int tile) {
+    const int key0 = k0 + tile * KT;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)key0 * DHM * 2), (short)0,
+                                             (S.ctx - key0) * DHM * 2, 0x00020000);
+  };
+  auto issue_k = [&](int tile, unsigned char* slot) {
+    if (tile >= ntiles) return;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(khead, tile);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = wave + 8 * j;
-      const int key = full ? kt + dkey[j] : min(kt + dkey[j], k1 - 1);  // clamped rows masked
-      __builtin_amdgcn_global_load_lds((const void*)(dsrc[j] + (size_t)key * DHM),
-                                       (void*)(&ring[slot][q >> 4][(q & 15) * 1024]), 16, 0, 0);
-    }
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(slot + (wave + 8 * j) * 1024), 16, kvo[j],
+          0, 0, 0);
+  };
+  auto issue_v = [&](int tile, unsigned char* slot) {
+    if (tile >= ntiles) return;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vhead, tile);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(slot + (wave + 8 * j) * 1024), 16, vvo[j],
+          0, 0, 0);
   };
 
   f32x16 o[4];
@@ -243,7 +283,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   float m = -INFINITY, lsum = 0.f;  // m: reference max of raw scores, shared by lanes l, l^32
   const float thresh = RESCALE_LOG2 / cs;
 
-  // Loop-invariant LDS byte offsets within a stage.  K read for K-step ks of key l32 (+32 per
+  // Loop-invariant LDS byte offsets within a slot.  K read for K-step ks of key l32 (+32 per
   // key block): chunk 2ks + hi in slot chunk ^ (key & 15).  V^T read (transposing) of lane
   // (g = lane/16, e = (lane/4)%4, q = lane%4) for dh block db: key 4*(g/2) + e (+ the key
   // offset of the MFMA step, a multiple of 8), dh 32db + 16(g%2) + 4q, i.e. chunk
@@ -264,47 +304,84 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   ones2[0] = (bf16)1.f;
   ones2[1] = (bf16)1.f;
 
+  // Per-lane LDS addresses of the V reads in slot 0 of the V ring.  The ring sits above
+  // 64 KB, past the reach of the 16-bit instruction offset, so the ring base is folded into
+  // the (opaque) register once and slot, key-group and half offsets stay immediates.
+  const lds_u8* vbase[4];
 #pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < ntiles) issue(p, p);
-
-  for (int it = 0; it < ntiles; ++it) {
-    attn_wait_vmcnt(4 * min(NST - 2, ntiles - 1 - it));  // this wave's part of tile `it`
-    asm volatile("s_barrier" ::: "memory");              // ... and everybody else's
-    if (it + NST - 1 < ntiles) issue(it + NST - 1, (it + NST - 1) % NST);
-    const int kt = k0 + it * KT;
-    const unsigned char* stage = &ring[it % NST][0][0];
-
-    // scores: two 32-key blocks; lane holds query l32, keys 8*(r/4) + 4*hi + r%4
-    f32x16 sacc[2];
+  for (int db = 0; db < 4; ++db) {
+    unsigned a32 = (unsigned)(size_t)(const lds_u8*)&vring[0][0] + (unsigned)voff[db];
+    asm volatile("" : "+v"(a32));
+    vbase[db] = (const lds_u8*)(size_t)a32;
+  }
+  // P.V of group g (keys 16g .. 16g+15 of the tile) for the four 32-row dh blocks; J = slot
+  auto pv_group = [&](int J, int g, const bf16x8& pf) {
+    const int kofs = J * TILE_BYTES + ((g >> 1) * 32 + 16 * (g & 1)) * 256;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int db = 0; db < 4; ++db) {
+      const s16x4 lo = lds_read_tr16(vbase[db] + kofs);
+      const s16x4 hv = lds_read_tr16(vbase[db] + kofs + 8 * 256);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
+    }
+  };
+  // scores of K-steps 2g, 2g+1 for both 32-key blocks
+  auto qk_steps = [&](const unsigned char* kst, int g, f32x16 (&sc)[2]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const unsigned char* kp = stage + koff[ks];
+    for (int ks = 2 * g; ks < 2 * g + 2; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)(kp + kb * 32 * 256);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
+        const bf16x8 kf = *(const bf16x8*)(kst + koff[ks] + kb * 32 * 256);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
       }
+  };
+  // probabilities of group g with reference mc; lane holds keys 8*(r/4) + 4*hi + r%4 of the
+  // 32-key block g/2, r = 8*(g%2) .. +7; returns their sum (of the rounded values)
+  auto probs = [&](const f32x16 (&sc)[2], int g, float mc, bf16x8& pf) {
+    float l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pf[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[g >> 1][8 * (g & 1) + e], cs, -mc));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2 pp;
+      pp[0] = pf[e];
+      pp[1] = pf[e + 1];
+      l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l, false);
     }
+    return l;
+  };
+
+  // One tile of the software pipeline; J = it % NR is a compile-time constant so every LDS
+  // address is a per-lane register plus an immediate.  K(t) lives in kring[t % NR] and V(t)
+  // in vring[t % NR]; iteration it reads K(it+1) and V(it) and refills the slots of K(it-1)
+  // and V(it-2) with K(it+3) and V(it+2).  Issue order: K(0) K(1) V(0) in the prologue,
+  // then K(t+2) V(t+1) "in iteration t-1" (t = 0: the prologue's tail), so the loads issued
+  // after those iteration it needs are exactly the previous iteration's K(it+2) and V(it+1).
+  // (Fetching one more tile ahead measured slightly slower.)
+  auto step = [&](auto Jc, int it, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+    constexpr int J = decltype(Jc)::value;
+    attn_wait_vmcnt(2 * (it + 2 < ntiles) + 2 * (it + 1 < ntiles));  // K(it+1), V(it)
+    asm volatile("s_barrier" ::: "memory");  // every wave's part landed; old slots free
+    issue_k(it + 3, &kring[(J + 3) % NR][0]);
+    issue_v(it + 2, &vring[(J + 2) % NR][0]);
+    if (!wactive) return;
+    const int kt = k0 + it * KT;
     if (kt + KT > k1) {  // ragged last tile (uniform branch)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= k1) sacc[kb][r] = -INFINITY;
+          if (key >= k1) scur[kb][r] = -INFINITY;
         }
     }
-    float mt = sacc[0][0];
+    float mt = scur[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[0][r]);
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, scur[0][r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[1][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, scur[1][r]);
+    mt = pair_max(mt);
     if (__builtin_amdgcn_ballot_w64(mt > m + thresh) != 0) {  // some reference too low: raise
       const float mn = mt > m + thresh ? mt : m;
       const float corr = __builtin_amdgcn_exp2f((m - mn) * cs);
@@ -316,42 +393,53 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       m = mn;
     }
     const float mc = m * cs;
+    // K(it+1) is stale past the last tile; those scores are never used
+    const unsigned char* kst = &kring[(J + 1) % NR][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) snext[kb][r] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      qk_steps(kst, g, snext);
+      bf16x8 pf;
+      lsum += probs(scur, g, mc, pf);
+      pv_group(J, g, pf);
+    }
+  };
 
-    const unsigned char* vp[4];
+  f32x16 sa[2], sb[2];
+  if (ntiles > 0) {
+    issue_k(0, &kring[0][0]);
+    issue_k(1, &kring[1][0]);
+    issue_v(0, &vring[0][0]);
+    issue_k(2, &kring[2][0]);
+    issue_v(1, &vring[1][0]);
+    // this wave's part of K(0): K(1), V(0), K(2), V(1) may still be in flight
+    attn_wait_vmcnt(2 * (ntiles > 1) + 2 + 2 * (ntiles > 2) + 2 * (ntiles > 1));
+    asm volatile("s_barrier" ::: "memory");  // ... and everybody else's part
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vp[db] = stage + KT * 256 + voff[db];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
+    if (wactive) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * st + e], cs, -mc));
-        // the denominator sums exactly the rounded p that enter the P.V product
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          bf16x2 pp;
-          pp[0] = pf[e];
-          pp[1] = pf[e + 1];
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, lsum, false);
-        }
-        // V^T operand rows dh = 32db + l32, keys kb*32 + 16st + 4hi + (0..3, 8..11)
-        const int kofs = (kb * 32 + 16 * st) * 256;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const s16x4 lo = lds_read_tr16(vp[db] + kofs);
-          const s16x4 hv = lds_read_tr16(vp[db] + kofs + 8 * 256);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
-        }
-      }
+      for (int g = 0; g < 4; ++g) qk_steps(&kring[0][0], g, sa);
     }
   }
-  lsum += __shfl_xor(lsum, 32, 64);
+  static_assert(NR == 4, "the main loop is unrolled by the ring size");
+  for (int it = 0; it < ntiles; it += NR) {
+    step(std::integral_constant<int, 0>{}, it, sa, sb);
+    if (it + 1 >= ntiles) break;
+    step(std::integral_constant<int, 1>{}, it + 1, sb, sa);
+    if (it + 2 >= ntiles) break;
+    step(std::integral_constant<int, 2>{}, it + 2, sa, sb);
+    if (it + 3 >= ntiles) break;
+    step(std::integral_constant<int, 3>{}, it + 3, sb, sa);
+  }
+  lsum = pair_sum(lsum);
   if (!tvalid) return;
-  const size_t qrow = (size_t)row * a.hq + h;
-  const size_t slot = (size_t)sp * a.Rtot * a.hq + qrow;
+  const size_t slot = attn_slot(S, sp, tt / G, a.hq, h);
   float* op = a.Opart + slot * DHM;
   // O^T accumulator: lane holds dh = 32*db + 8*(r/4) + 4*hi + r%4 of query l32
 #pragma unroll
@@ -375,8 +463,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------
 // combine: one wave per (row, query head).  All maxima are in the log2 domain.
 // ------------------------------------------------------------------------------------
-template <class T>
+template <class T, int DH>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int EPL = DH / 64;  // consecutive dh elements per lane
   const int widx = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (widx >= a.R * a.hq) return;
   const int lane = threadIdx.x & 63;
@@ -384,38 +473,58 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int G = a.hq / a.hkv;
   const int c = h / G;
   const AttnSeq S = a.seqs[a.row_seq[r]];
-  const T* q = (const T*)a.Q + ((size_t)r * a.hq + h) * a.dh;
-  const float* ks = a.kself + ((size_t)r * a.hkv + c) * a.dh;
-  const float* vs = a.vself + ((size_t)r * a.hkv + c) * a.dh;
+  const int e0 = lane * EPL;
+  const T* q = (const T*)a.Q + ((size_t)r * a.hq + h) * DH + e0;
+  const float* ks = a.kself + ((size_t)r * a.hkv + c) * DH + e0;
+  const float* vs = a.vself + ((size_t)r * a.hkv + c) * DH + e0;
   float d = 0.f;
-  for (int e = lane; e < a.dh; e += 64) d = fmaf(to_f32(q[e]), ks[e], d);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) d = fmaf(to_f32(q[e]), ks[e], d);
   const float s_self = warp_sum(d) * a.scale_log2;
   const size_t qrow = (size_t)r * a.hq + h;
-  const size_t split_stride = (size_t)a.R * a.hq;
+  const int rl = r - S.row_off;
+  const size_t slot0 = attn_slot(S, 0, rl, a.hq, h);
+  const size_t split_stride = (size_t)S.M * a.hq;
+  const int ns = S.nsplit;
   // lane sp < nsplit holds split sp's (max, denominator); weights 2^(m_sp - M)
-  const bool has = lane < S.nsplit;
-  const float ms = has ? a.Mpart[lane * split_stride + qrow] : -INFINITY;
-  const float ls = has ? a.Lpart[lane * split_stride + qrow] : 0.f;
+  const bool has = lane < ns;
+  const float ms = has ? a.Mpart[slot0 + lane * split_stride] : -INFINITY;
+  const float ls = has ? a.Lpart[slot0 + lane * split_stride] : 0.f;
   const float mx = fmaxf(warp_max(ms), s_self);
   const float wsp = has ? exp2f(ms - mx) : 0.f;
   const float w_self = exp2f(s_self - mx);
   const float den = warp_sum(wsp * ls) + w_self;
   const float inv = 1.0f / den;
-  T* out = (T*)a.O + qrow * a.dh;
-  for (int e = lane; e < a.dh; e += 64) {
-    float num = w_self * vs[e];
-    for (int sp = 0; sp < S.nsplit; ++sp) {
-      const float w = __shfl(wsp, sp, 64);
-      num = fmaf(w, a.Opart[(sp * split_stride + qrow) * a.dh + e], num);
+  float num[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) num[e] = w_self * vs[e];
+  // splits in groups of 8 with the loads of a group issued together (fixed summation order)
+  const float* op = a.Opart + slot0 * DH + e0;
+  for (int sp0 = 0; sp0 < ns; sp0 += 8) {
+    float v[8][EPL];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float* pj = op + (size_t)(sp0 + j) * split_stride * DH;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[j][e] = sp0 + j < ns ? pj[e] : 0.f;
     }
-    out[e] = from_f32<T>(num * inv);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), min(sp0 + j, 63)));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, v[j][e], num[e]);
+    }
   }
+  T* out = (T*)a.O + qrow * DH + e0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) out[e] = from_f32<T>(num[e] * inv);
 }
 
 }  // namespace
 
 int attention_qblock(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? QB : 64; }
-int attention_target_wgs(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? 256 : 1024; }
+// MFMA kernel: 128 KB of LDS rings -> one per CU; VALU kernel: 64 threads, <= 33 KB LDS
+int attention_wgs_per_cu(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? 1 : 4; }
 
 hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s) {
   const int waves = a.R * (a.hq + 2 * a.hkv);
@@ -448,10 +557,18 @@ hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t 
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s) {
   const int waves = a.R * a.hq;
   const dim3 grid((waves + 3) / 4), block(256);
-  if (act == ACT_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, block, 0, s, a);
+  if (a.dh != 64 && a.dh != 128) return hipErrorInvalidValue;
+  if (act == ACT_F32) {
+    if (a.dh == 64)
+      hipLaunchKernelGGL((combine_kernel<float, 64>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, 128>), grid, block, 0, s, a);
+  } else {
+    if (a.dh == 64)
+      hipLaunchKernelGGL((combine_kernel<bf16, 64>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<bf16, 128>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -57,17 +57,25 @@ struct AttnSeq {
   int M;          // rows of the sequence in this item (live sources + reference)
   int nsplit;     // context splits
   int chunk;      // positions per split (multiple of 64)
+  int part_off;   // first partial slot of the sequence; slot of (split sp, local row r,
+                  // head h) = part_off + (sp * M + r) * hq + h
+  int pad0, pad1, pad2;
 };
+
+// Partial-result slot of one (split, row, query head) of a sequence.
+__host__ __device__ inline size_t attn_slot(const AttnSeq& s, int sp, int r_local, int hq,
+                                            int h) {
+  return (size_t)s.part_off + ((size_t)sp * s.M + r_local) * hq + h;
+}
 
 struct AttnArgs {
   const void* Q;       // [R][hq][dh] activations (position-rotated, unscaled)
   int hq, hkv, dh;
-  const int4* work;    // per workgroup: (seq, kv head, q block, split)
+  const int4* work;    // per workgroup: (seq, kv head, q block, split); seq < 0: no work
   const AttnSeq* seqs; // [n_seqs]
-  float* Opart;        // [max_split][R*hq][dh] unnormalised partial outputs
-  float* Mpart;        // [max_split][R*hq] running max (log2 domain)
-  float* Lpart;        // [max_split][R*hq] partial denominators
-  int Rtot;
+  float* Opart;        // [slots][dh] unnormalised partial outputs
+  float* Mpart;        // [slots] running max (log2 domain)
+  float* Lpart;        // [slots] partial denominators
   float scale_log2;    // log2(e) / sqrt(dh)
 };
 
@@ -164,7 +172,7 @@ hipError_t launch_init(const InitArgs& a, hipStream_t s);
 
 // rows of Q per attention workgroup for the given activation type / head size
 int attention_qblock(int act, int dh);
-// workgroups the context splits should fill per attention launch
-int attention_target_wgs(int act, int dh);
+// attention workgroups resident per compute unit (LDS / register limited)
+int attention_wgs_per_cu(int act, int dh);
 
 }  // namespace ks

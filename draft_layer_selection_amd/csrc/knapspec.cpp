@@ -39,7 +39,8 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int PSPLIT_MAX = 8;    // K splits of the partial-output GEMMs
-constexpr int ASPLIT_MAX = 16;   // context splits of the attention
+constexpr int ASPLIT_MAX = 32;   // context splits of the attention (combine: <= 64)
+constexpr int N_XCD = 8;         // accelerator complex dies; workgroup i runs on die i % 8
 constexpr int MAX_BUDGETS = 1024;
 constexpr int GAMMA_LIMIT = 64;
 constexpr size_t ALIGN = 256;
@@ -55,7 +56,8 @@ struct Carver {
   }
 };
 
-// Byte offsets of the per-solve map / launch tables (same layout on host and device).
+// Byte offsets of the per-solve map / launch tables (same layout on host and device).  The
+// attention work lists come last so that a solve uploads only the part it filled.
 struct MapLayout {
   size_t exec, next, rowseq, rowstate, info, work, aseq, rope, x0, init, total, max_work;
 };
@@ -69,14 +71,64 @@ MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int
   L.rowseq = c.take((size_t)L2 * Rmax * 4);
   L.rowstate = c.take((size_t)L2 * Rmax * 4);
   L.info = c.take((size_t)L2 * S * sizeof(ks::ItemSeq));
-  L.max_work = (size_t)n_layers * S * hkv * ((G * Bm + 63) / 64) * asplit_max;
-  L.work = c.take(L.max_work * 16);
   L.aseq = c.take((size_t)n_layers * S * sizeof(ks::AttnSeq));
   L.rope = c.take(S * dh * 4);
   L.x0 = c.take(S * 8);
   L.init = c.take(S * 2 * 4);
+  // per layer: every (sequence, KV head, query block, split) once, plus the empty entries
+  // that keep each die's share of the list aligned (at most one query-block group per die)
+  const size_t qb_max = (G * (Bm + 1) + 63) / 64;
+  L.max_work = (size_t)n_layers * (S * hkv * qb_max * asplit_max + N_XCD * qb_max);
+  L.work = c.take(L.max_work * 16);
   L.total = c.off;
   return L;
+}
+
+// Context splits of one attention item.  Sequence q has pairs[q] (KV head, query block)
+// pairs, each streaming tiles[q] 64-key tiles of its cache, and rows[q] query rows x heads.
+// A common cap X on the tiles per workgroup gives nsplit_q = ceil(tiles_q / X); X is chosen
+// to minimise (dispatch rounds) x (X + ATTN_WG_FIXED_TILES), rounds = ceil(workgroups /
+// slots), ties to fewer workgroups, with at most max_split splits per sequence and at most
+// part_cap partial slots.
+constexpr long ATTN_WG_FIXED_TILES = 4;  // pipeline fill + the partial-result write of a
+                                         // workgroup (256 rows x 512 B ~ 4 tiles of traffic)
+void plan_attention_splits(const std::vector<int>& pairs, const std::vector<int>& tiles,
+                           const std::vector<size_t>& rows, int slots, int max_split,
+                           size_t part_cap, std::vector<int>& nsplit) {
+  const size_t n = pairs.size();
+  nsplit.assign(n, 0);
+  int xmin = 1, tmax = 0;
+  for (size_t q = 0; q < n; ++q) {
+    if (tiles[q] <= 0) continue;
+    xmin = std::max(xmin, (tiles[q] + max_split - 1) / max_split);
+    tmax = std::max(tmax, tiles[q]);
+  }
+  if (tmax == 0) return;
+  long best_cost = -1, best_count = 0;
+  int best_x = tmax;
+  auto consider = [&](int x) {
+    if (x < xmin || x > tmax) return;
+    long count = 0;
+    size_t parts = 0;
+    for (size_t q = 0; q < n; ++q) {
+      if (tiles[q] <= 0) continue;
+      const int ns = (tiles[q] + x - 1) / x;
+      count += (long)pairs[q] * ns;
+      parts += rows[q] * ns;
+    }
+    if (parts > part_cap && x != tmax) return;
+    const long cost = (count + slots - 1) / slots * (x + ATTN_WG_FIXED_TILES);
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && count < best_count)) {
+      best_cost = cost;
+      best_count = count;
+      best_x = x;
+    }
+  };
+  consider(tmax);
+  for (size_t q = 0; q < n; ++q)
+    for (int k = 1; k <= max_split && tiles[q] > 0; ++k) consider((tiles[q] + k - 1) / k);
+  for (size_t q = 0; q < n; ++q)
+    if (tiles[q] > 0) nsplit[q] = (tiles[q] + best_x - 1) / best_x;
 }
 
 }  // namespace
@@ -94,6 +146,8 @@ struct knapspec_model {
   // dimensions
   int L2 = 0, mw = 0, qdim = 0, kvdim = 0, nqkv = 0, Rmax = 0;
   size_t p_floats = 0;
+  size_t part_slots = 0;  // attention partial results: (split, row, query head) slots
+  int n_cus = 0;
 
   // device workspace
   char* ws = nullptr;
@@ -337,9 +391,13 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   m->desc = d;
   m->act = d.dtype == KNAPSPEC_BF16 ? ks::ACT_BF16 : ks::ACT_F32;
   m->elem = d.dtype == KNAPSPEC_BF16 ? 2 : 4;
-  if (hipGetDevice(&m->device) != hipSuccess) {
+  if (hipGetDevice(&m->device) != hipSuccess ||
+      hipDeviceGetAttribute(&m->n_cus, hipDeviceAttributeMultiprocessorCount, m->device) !=
+          hipSuccess ||
+      m->n_cus <= 0) {
+    (void)hipGetLastError();
     delete m;
-    return fail(KNAPSPEC_EHIP, "hipGetDevice failed");
+    return fail(KNAPSPEC_EHIP, "hipGetDevice / compute-unit count query failed");
   }
   m->layers.assign(layers, layers + d.n_layers);
   m->L2 = 2 * d.n_layers;
@@ -365,9 +423,10 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   const size_t o_h = c.take(R * d.d_ff * m->elem);
   const size_t o_P = c.take(m->p_floats * 4);
   const size_t o_E = c.take(R * D * 4);
-  const size_t o_Op = c.take((size_t)ASPLIT_MAX * R * m->qdim * 4);
-  const size_t o_Mp = c.take((size_t)ASPLIT_MAX * R * d.n_q_heads * 4);
-  const size_t o_Lp = c.take((size_t)ASPLIT_MAX * R * d.n_q_heads * 4);
+  m->part_slots = (size_t)d.n_q_heads * std::max<size_t>(ASPLIT_MAX * std::min<size_t>(R, 512), R);
+  const size_t o_Op = c.take(m->part_slots * d.head_dim * 4);
+  const size_t o_Mp = c.take(m->part_slots * 4);
+  const size_t o_Lp = c.take(m->part_slots * 4);
   const size_t o_dec = c.take(S * m->L2 * Bm);
   const size_t o_mar = c.take(S * m->L2 * Bm * 4);
   const size_t o_cos = c.take(S * Bm * 4);
@@ -644,45 +703,69 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       }
     }
   }
-  // attention work lists, one per attention item, in item order
+  // attention work lists, one per attention item, in item order.  The query blocks of one
+  // (sequence, KV head, split) read the same keys and values: they are placed on one die
+  // (list positions congruent mod N_XCD) so the die's L2 serves the repeated reads; the
+  // other dies' positions in a round are filled with empty entries.
   std::vector<int> work_off(d.n_layers), work_cnt(d.n_layers);
   size_t nw = 0;
-  for (int l = 0; l < d.n_layers; ++l) {
-    const int i = 2 * l;
-    int base = 0;
-    for (int q = 0; q < S; ++q)
-      base += hkv * (int)((G * (plan[q].src[i].size() + 1) + qb_rows - 1) / qb_rows);
-    const int target = ks::attention_target_wgs(m->act, dh);
-    work_off[l] = (int)nw;
-    for (int q = 0; q < S; ++q) {
-      const knapspec_seq& sq = args->seqs[q];
-      const int M = (int)plan[q].src[i].size() + 1;
-      const int qblocks = (int)((G * M + qb_rows - 1) / qb_rows);
-      const int ctx = sq.ctx_len;
-      int nsplit = 0, chunk = 64;
-      if (ctx > 0) {
-        int want = std::max(1, (target + base - 1) / base);
-        want = std::min(want, ASPLIT_MAX);
-        want = std::min(want, std::max(1, ctx / 256));
-        chunk = (((ctx + want - 1) / want) + 63) / 64 * 64;
-        nsplit = (ctx + chunk - 1) / chunk;
+  {
+    const int slots = m->n_cus * ks::attention_wgs_per_cu(m->act, dh);
+    std::vector<int> pairs(S), tiles(S), qblocks(S), nsplit;
+    std::vector<size_t> prow(S);
+    std::vector<std::vector<int4>> die(N_XCD);
+    for (int l = 0; l < d.n_layers; ++l) {
+      const int i = 2 * l;
+      for (int q = 0; q < S; ++q) {
+        const int M = (int)plan[q].src[i].size() + 1;
+        qblocks[q] = (int)((G * M + qb_rows - 1) / qb_rows);
+        pairs[q] = hkv * qblocks[q];
+        tiles[q] = (args->seqs[q].ctx_len + 63) / 64;
+        prow[q] = (size_t)M * hq;
       }
-      ks::AttnSeq& as = aseq[(size_t)l * S + q];
-      as.k = ctx > 0 ? sq.k_cache[l] : nullptr;
-      as.v = ctx > 0 ? sq.v_cache[l] : nullptr;
-      as.ctx = ctx;
-      as.cap = sq.ctx_capacity;
-      as.row_off = row_off[(size_t)i * S + q];
-      as.M = M;
-      as.nsplit = nsplit;
-      as.chunk = chunk;
-      for (int c = 0; c < hkv; ++c)
-        for (int qb = 0; qb < qblocks; ++qb)
-          for (int sp = 0; sp < nsplit; ++sp) work[nw++] = make_int4(q, c, qb, sp);
+      plan_attention_splits(pairs, tiles, prow, slots, ASPLIT_MAX, m->part_slots, nsplit);
+      size_t part = 0;
+      for (auto& v : die) v.clear();
+      std::vector<size_t> load(N_XCD, 0);
+      for (int q = 0; q < S; ++q) {
+        const knapspec_seq& sq = args->seqs[q];
+        const int M = (int)plan[q].src[i].size() + 1;
+        const int ctx = sq.ctx_len;
+        const int ns = nsplit[q];
+        const int chunk = ns > 0 ? (tiles[q] + ns - 1) / ns * 64 : 64;
+        ks::AttnSeq& as = aseq[(size_t)l * S + q];
+        as.k = ctx > 0 ? sq.k_cache[l] : nullptr;
+        as.v = ctx > 0 ? sq.v_cache[l] : nullptr;
+        as.ctx = ctx;
+        as.cap = sq.ctx_capacity;
+        as.row_off = row_off[(size_t)i * S + q];
+        as.M = M;
+        as.nsplit = ctx > 0 ? (ctx + chunk - 1) / chunk : 0;
+        as.chunk = chunk;
+        as.part_off = (int)part;
+        as.pad0 = as.pad1 = as.pad2 = 0;
+        part += (size_t)as.nsplit * M * hq;
+        for (int c = 0; c < hkv; ++c)
+          for (int sp = 0; sp < as.nsplit; ++sp) {
+            const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+            for (int qb = 0; qb < qblocks[q]; ++qb) die[x].push_back(make_int4(q, c, qb, sp));
+            load[x] += qblocks[q];
+          }
+      }
+      if (part > m->part_slots)
+        return fail(KNAPSPEC_EINVAL, "internal: attention partial slots overflow");
+      work_off[l] = (int)nw;
+      const size_t rounds = *std::max_element(load.begin(), load.end());
+      if (nw + rounds * N_XCD > max_work)
+        return fail(KNAPSPEC_EINVAL, "internal: attention work list overflow");
+      for (size_t j = 0; j < rounds; ++j)
+        for (int x = 0; x < N_XCD; ++x)
+          work[nw++] = j < die[x].size() ? die[x][j] : make_int4(-1, 0, 0, 0);
+      // drop the trailing empty entries of the last round
+      while (nw > (size_t)work_off[l] && work[nw - 1].x < 0) --nw;
+      work_cnt[l] = (int)nw - work_off[l];
     }
-    work_cnt[l] = (int)nw - work_off[l];
   }
-  if (nw > max_work) return fail(KNAPSPEC_EINVAL, "internal: attention work list overflow");
   // RoPE table at position ctx_len of each sequence: angle_j = n * theta^(-2j/dh) in float64
   for (int q = 0; q < S; ++q) {
     const double n = (double)args->seqs[q].ctx_len;
@@ -710,7 +793,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   // All device work of one solve, enqueued on `st`: map upload, the DP, result copies.
   auto enqueue = [&](hipStream_t st) -> int {
   char* dm = m->maps;
-  HIPCHK(hipMemcpyAsync(dm, hm, ml.total, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(dm, hm, o_work + nw * sizeof(int4), hipMemcpyHostToDevice, st));
   const int32_t* d_exec = (const int32_t*)(dm + o_exec);
   const int32_t* d_next = (const int32_t*)(dm + o_next);
   const int32_t* d_rowseq = (const int32_t*)(dm + o_rowseq);
@@ -809,7 +892,6 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       aa.Opart = m->Opart;
       aa.Mpart = m->Mpart;
       aa.Lpart = m->Lpart;
-      aa.Rtot = R;
       aa.scale_log2 = scale_log2;
       pk = prof_begin(m, KNAPSPEC_K_ATTENTION, st);
       HIPCHK(ks::launch_attention(aa, m->act, work_cnt[l], st));

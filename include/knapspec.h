@@ -59,10 +59,10 @@ typedef struct knapspec_model knapspec_model; /* opaque */
 /* Decoder shape and the limits the library sizes its device workspace for. */
 typedef struct {
   int32_t n_layers;    /* L; the DP has 2L items */
-  int32_t d_model;     /* hidden size d */
+  int32_t d_model;     /* hidden size d (a multiple of 4; bf16: of 64) */
   int32_t n_q_heads;   /* hq */
   int32_t n_kv_heads;  /* hkv, divides hq; query head h reads KV head h / (hq/hkv) */
-  int32_t head_dim;    /* dh (64 or 128 for bf16; any even value <= 128 for f32) */
+  int32_t head_dim;    /* dh: 64 or 128 */
   int32_t d_ff;        /* SwiGLU inner size */
   int32_t dtype;       /* KNAPSPEC_F32 or KNAPSPEC_BF16 */
   float rms_eps;       /* RMSNorm epsilon */
@@ -176,7 +176,7 @@ int knapspec_item_weights(const knapspec_latency_model* lat, int32_t n_layers, i
 #define KNAPSPEC_K_GEMM_O 5
 #define KNAPSPEC_K_GEMM_GATE_UP 6
 #define KNAPSPEC_K_GEMM_DOWN 7
-#define KNAPSPEC_K_SELECT 8
+#define KNAPSPEC_K_SELECT 8 /* split/residual reduce + cosine select + next-item RMSNorm */
 int knapspec_set_profiling(knapspec_model* model, int32_t enable);
 int knapspec_get_kernel_times(const knapspec_model* model, double* total_ms, int64_t* launches,
                               int32_t n_classes);
