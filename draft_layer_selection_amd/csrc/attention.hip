@@ -143,10 +143,10 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------
 // MFMA attention partial (bf16, dh = 128): 8 waves x 32 query rows = 256 query rows per
 // workgroup (one workgroup per CU), 64-key tiles.
-//   * K and V tiles go global -> LDS with global_load_lds_dwordx4 (1 KB = 4 keys x 256 B per
-//     wave instruction) into a K ring and a V ring of four slots each, both kept as
-//     [key][dh]; the barrier between tiles is a bare s_barrier after a per-wave vmcnt wait (a
-//     fenced barrier would drain the tiles in flight).
+//   * K and V tiles are loaded with range-checked 16-byte buffer loads into registers one
+//     iteration ahead and stored to a K ring and a V ring of four slots each, both kept as
+//     [key][dh] (measured faster than loading global -> LDS directly, which competes with the
+//     LDS reads of the MFMA operands).
 //   * LDS has 64 banks x 4 B.  K: 16-byte chunk c of key k lives in slot c ^ (k & 15), so the
 //     16-byte reads of 16 consecutive keys are conflict-free.  V: chunk c of key k lives in
 //     slot c ^ (4 * (k & 3)), so the transposing reads below are conflict-free.
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 //     only when a score exceeds it by more than 2^8 in p); exact because l carries the same m.
 //   * Software pipeline: iteration t issues the score MFMAs of tile t+1 between the
 //     exponentials and P.V MFMAs of tile t, so one wave keeps the matrix core and the vector
-//     ALU busy at once.  K of tile t is read in iteration t-1 and V in iteration t, so
-//     K(t+3) and V(t+2) are fetched in iteration t, two iterations ahead of use.
+//     ALU busy at once.  K of tile t is read in iteration t-1 and V in iteration t; tile t is
+//     loaded in iteration t-3 and stored to LDS in iteration t-2.
 // ------------------------------------------------------------------------------------
 constexpr int DHM = 128;
 constexpr int KT = 64;                 // keys per tile
@@ -191,19 +191,14 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// s_waitcnt with vmcnt = n (even n <= 14; anything else waits for all) and no wait on the
-// other counters (gfx9 encoding: vmcnt low bits [3:0], expcnt [6:4], lgkmcnt [11:8])
-__device__ __forceinline__ void attn_wait_vmcnt(int n) {
-  switch (n) {
-    case 14: __builtin_amdgcn_s_waitcnt(14 | (7 << 4) | (15 << 8)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8)); break;
-    default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
-  }
+// s_waitcnt with vmcnt = 0 only, and with lgkmcnt = 0 only (gfx9 encoding: vmcnt bits [3:0]
+// and [15:14], expcnt [6:4], lgkmcnt [11:8]); the barrier between tiles is a bare s_barrier
+// after these, since __syncthreads would also drain the staged loads in flight
+__device__ __forceinline__ void attn_wait_vmcnt(int) {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void attn_wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
@@ -236,8 +231,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char kring[NR][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char vring[NR][TILE_BYTES];
 
-  // DMA: a tile is 16 chunks of 4 keys of K and 16 of V; wave w issues chunks w and w + 8 of
-  // each.  Lane -> key 4*chunk + lane/16 of the tile, LDS slot lane%16 <- global 16-byte
+  // Loads: a tile is 16 chunks of 4 keys of K and 16 of V; wave w moves chunks w and w + 8
+  // of each.  Lane -> key 4*chunk + lane/16 of the tile, LDS slot lane%16 <- global 16-byte
   // chunk slot ^ swz(key), swz = key & 15 for K and 4*(key & 3) for V.  The loads are
   // range-checked buffer loads whose resource starts at the tile's first key and ends at the
   // sequence's last cached key: keys past the cache read as zeros (their scores are masked),
@@ -256,23 +251,26 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)key0 * DHM * 2), (short)0,
                                              (S.ctx - key0) * DHM * 2, 0x00020000);
   };
-  auto issue_k = [&](int tile, unsigned char* slot) {
+  // one tile is staged through registers: loaded in one iteration, stored to LDS in the next
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 stg[4];  // this lane's K (0, 1) and V (2, 3) chunks of the staged tile
+  auto load_tile = [&](int tile) {
     if (tile >= ntiles) return;
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(khead, tile);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(khead, tile);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vhead, tile);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(slot + (wave + 8 * j) * 1024), 16, kvo[j],
-          0, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      stg[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, kvo[j], 0, 0);
+      stg[2 + j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vvo[j], 0, 0);
+    }
   };
-  auto issue_v = [&](int tile, unsigned char* slot) {
+  auto store_tile = [&](int tile, int slot) {
     if (tile >= ntiles) return;
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vhead, tile);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(slot + (wave + 8 * j) * 1024), 16, vvo[j],
-          0, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      *(u32x4*)&kring[slot][(wave + 8 * j) * 1024 + lane * 16] = stg[j];
+      *(u32x4*)&vring[slot][(wave + 8 * j) * 1024 + lane * 16] = stg[2 + j];
+    }
   };
 
   f32x16 o[4];
@@ -353,18 +351,16 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   };
 
   // One tile of the software pipeline; J = it % NR is a compile-time constant so every LDS
-  // address is a per-lane register plus an immediate.  K(t) lives in kring[t % NR] and V(t)
-  // in vring[t % NR]; iteration it reads K(it+1) and V(it) and refills the slots of K(it-1)
-  // and V(it-2) with K(it+3) and V(it+2).  Issue order: K(0) K(1) V(0) in the prologue,
-  // then K(t+2) V(t+1) "in iteration t-1" (t = 0: the prologue's tail), so the loads issued
-  // after those iteration it needs are exactly the previous iteration's K(it+2) and V(it+1).
-  // (Fetching one more tile ahead measured slightly slower.)
+  // address is a per-lane register plus an immediate.  Tile t lives in kring/vring[t % NR];
+  // iteration it reads K(it+1) and V(it), stores the staged tile it+2 into the slot of tile
+  // it-2 (last read in iteration it-2) and loads tile it+3 into the staging registers.
   auto step = [&](auto Jc, int it, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
     constexpr int J = decltype(Jc)::value;
-    attn_wait_vmcnt(2 * (it + 2 < ntiles) + 2 * (it + 1 < ntiles));  // K(it+1), V(it)
-    asm volatile("s_barrier" ::: "memory");  // every wave's part landed; old slots free
-    issue_k(it + 3, &kring[(J + 3) % NR][0]);
-    issue_v(it + 2, &vring[(J + 2) % NR][0]);
+    attn_wait_lgkm0();                       // this wave's LDS stores of the last iteration
+    asm volatile("s_barrier" ::: "memory");  // ... and everyone's: K(it+1), V(it) visible
+    attn_wait_vmcnt(0);                      // the staged tile it+2 arrived
+    store_tile(it + 2, (J + 2) % NR);
+    load_tile(it + 3);
     if (!wactive) return;
     const int kt = k0 + it * KT;
     if (kt + KT > k1) {  // ragged last tile (uniform branch)
@@ -410,14 +406,15 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 
   f32x16 sa[2], sb[2];
   if (ntiles > 0) {
-    issue_k(0, &kring[0][0]);
-    issue_k(1, &kring[1][0]);
-    issue_v(0, &vring[0][0]);
-    issue_k(2, &kring[2][0]);
-    issue_v(1, &vring[1][0]);
-    // this wave's part of K(0): K(1), V(0), K(2), V(1) may still be in flight
-    attn_wait_vmcnt(2 * (ntiles > 1) + 2 + 2 * (ntiles > 2) + 2 * (ntiles > 1));
-    asm volatile("s_barrier" ::: "memory");  // ... and everybody else's part
+    load_tile(0);
+    attn_wait_vmcnt(0);
+    store_tile(0, 0);
+    load_tile(1);
+    attn_wait_vmcnt(0);
+    store_tile(1, 1);
+    load_tile(2);
+    attn_wait_lgkm0();
+    asm volatile("s_barrier" ::: "memory");  // tiles 0 and 1 in LDS
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

@@ -19,6 +19,7 @@
 // bf16 fallback (gemm_bf16_kernel): direct-to-register loads, 64-column tiles, any N % 64 == 0.
 // f32 path: plain LDS-tiled FMA kernel (the small float32 decoder only).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -28,6 +29,19 @@ namespace ks {
 namespace {
 
 constexpr int RED_PITCH = 64 + 4;
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
 
 // Sum the four waves' copies of one 32x64 block and write it out (PARTIAL or SWIGLU).
 template <class T>
@@ -204,7 +218,9 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
   const int rest = L / a.m_tiles;
   const int sp = rest % a.splits;
   const int nt = rest / a.splits;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index as a scalar: the per-wave load counts and waits below become scalar code
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int grp = wave / KSL, ksl = wave % KSL;
   const int row0 = mt * 32 * MB;
@@ -261,11 +277,14 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
   for (int p = 0; p < S - 1; ++p)
     if (p < nit) issue(p, p);
 
-  for (int it = 0; it < nit; ++it) {
+  // one 64-K stage; slot J is a compile-time constant (the loop below is unrolled by S), so
+  // the LDS addresses are per-lane registers plus immediates
+  auto stage = [&](auto Jc, int it) {
+    constexpr int J = decltype(Jc)::value;
     wait_vmcnt(min(S - 2, nit - 1 - it) * my_loads);  // this wave's part of stage `it` landed
     asm volatile("s_barrier" ::: "memory");            // ... and everyone else's
-    if (it + S - 1 < nit) issue(it + S - 1, (it + S - 1) % S);  // refill the slot freed above
-    const unsigned char* st = smem + (it % S) * STAGE;
+    if (it + S - 1 < nit) issue(it + S - 1, (J + S - 1) % S);  // refill the slot freed above
+    const unsigned char* st = smem + J * STAGE;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int c = 2 * (ksl * KSTEPS + ks) + hi;  // 16-byte chunk of this lane's K
@@ -286,6 +305,12 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
         acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], wf[1], acc[mb][1], 0, 0, 0);
       }
     }
+  };
+  for (int it = 0; it < nit; it += S) {
+    static_for<S>([&](auto Jc) {
+      constexpr int J = decltype(Jc)::value;
+      if (it + J < nit) stage(Jc, it + J);
+    });
   }
   __syncthreads();
 
