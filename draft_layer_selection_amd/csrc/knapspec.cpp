@@ -192,7 +192,17 @@ struct knapspec_model {
   char* h_out = nullptr;
   size_t h_out_bytes = 0;
 
+  // item latency profiling (knapspec_profile_items): small tables, allocated on first use
+  char* pr_dev = nullptr;
+  char* pr_host = nullptr;
+  size_t pr_bytes = 0;
+  hipEvent_t pr_ev[2] = {nullptr, nullptr};
+
   ~knapspec_model() {
+    for (hipEvent_t e : pr_ev)
+      if (e) (void)hipEventDestroy(e);
+    if (pr_dev) (void)hipFree(pr_dev);
+    if (pr_host) (void)hipHostFree(pr_host);
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
     if (gexec) (void)hipGraphExecDestroy(gexec);
     if (ev_in) (void)hipEventDestroy(ev_in);
@@ -1076,5 +1086,301 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
                     (size_t)B * 4);
     }
   }
+  return KNAPSPEC_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Item latency profiling: one decode token (M = 1) through the draft pass's items
+// ------------------------------------------------------------------------------------------
+namespace {
+
+double median_of(std::vector<double> v) {
+  std::sort(v.begin(), v.end());
+  const size_t n = v.size();
+  return n % 2 ? v[n / 2] : 0.5 * (v[n / 2 - 1] + v[n / 2]);
+}
+
+}  // namespace
+
+KS_API int knapspec_fit_latency(const int32_t* n, const double* t, int32_t count, double* a,
+                                double* b, double* r2) {
+  if (!n || !t || !a || !b || !r2) return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  if (count < 2) return fail(KNAPSPEC_EINVAL, "need at least 2 points");
+  double sn = 0, st = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!std::isfinite(t[i])) return fail(KNAPSPEC_EINVAL, "t[%d] is not finite", i);
+    sn += n[i];
+    st += t[i];
+  }
+  const double mn = sn / count, mt = st / count;
+  double snn = 0, snt = 0, stt = 0;
+  for (int i = 0; i < count; ++i) {
+    const double dn = n[i] - mn, dt = t[i] - mt;
+    snn += dn * dn;
+    snt += dn * dt;
+    stt += dt * dt;
+  }
+  if (!(snn > 0)) return fail(KNAPSPEC_EINVAL, "need at least 2 distinct n");
+  *b = snt / snn;
+  *a = mt - *b * mn;
+  // residual sum of squares of the fitted line over the total sum of squares
+  double rss = 0;
+  for (int i = 0; i < count; ++i) {
+    const double e = t[i] - (*a + *b * n[i]);
+    rss += e * e;
+  }
+  *r2 = stt > 0 ? 1.0 - rss / stt : 1.0;
+  return KNAPSPEC_OK;
+}
+
+KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
+                                  const int32_t* ctx_lens, int32_t n_ctx, int32_t reps,
+                                  void* hip_stream, double* attn_us, double* mlp_us) {
+  if (!m || !seq || !ctx_lens || !attn_us || !mlp_us)
+    return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  const knapspec_model_desc& d = m->desc;
+  if (n_ctx < 1 || n_ctx > 1024) return fail(KNAPSPEC_EINVAL, "n_ctx must be in [1, 1024]");
+  if (reps < 1 || reps > 10000) return fail(KNAPSPEC_EINVAL, "reps must be in [1, 10000]");
+  if (!seq->x0) return fail(KNAPSPEC_EINVAL, "x0 is NULL");
+  int max_n = 0;
+  for (int i = 0; i < n_ctx; ++i) {
+    if (ctx_lens[i] < 0 || ctx_lens[i] > d.max_ctx)
+      return fail(KNAPSPEC_EINVAL, "ctx_lens[%d] must be in [0, %d]", i, d.max_ctx);
+    max_n = std::max(max_n, (int)ctx_lens[i]);
+  }
+  if (seq->ctx_capacity < max_n) return fail(KNAPSPEC_EINVAL, "ctx_capacity < max(ctx_lens)");
+  if (max_n > 0) {
+    if (!seq->k_cache || !seq->v_cache) return fail(KNAPSPEC_EINVAL, "cache arrays NULL");
+    for (int l = 0; l < d.n_layers; ++l)
+      if (!seq->k_cache[l] || !seq->v_cache[l])
+        return fail(KNAPSPEC_EINVAL, "layer %d: NULL cache pointer", l);
+  }
+  int cur_dev = -1;
+  if (hipGetDevice(&cur_dev) != hipSuccess || cur_dev != m->device)
+    return fail(KNAPSPEC_EINVAL, "current HIP device differs from the model's device");
+
+  const int hq = d.n_q_heads, hkv = d.n_kv_heads, dh = d.head_dim, D = d.d_model;
+  // table layout: rope [dh] f32 | row_seq, row_state [1] i32 | init rows [2] | x0 ptr |
+  // AttnSeq | work list
+  Carver c;
+  const size_t o_rope = c.take(dh * 4);
+  const size_t o_rowseq = c.take(4);
+  const size_t o_rowstate = c.take(4);
+  const size_t o_init = c.take(8);
+  const size_t o_x0 = c.take(8);
+  const size_t o_aseq = c.take(sizeof(ks::AttnSeq));
+  const size_t max_work = (size_t)hkv * ASPLIT_MAX;
+  const size_t o_work = c.take(max_work * sizeof(int4));
+  const size_t bytes = c.off;
+  if (m->pr_bytes < bytes) {
+    if (m->pr_dev) (void)hipFree(m->pr_dev);
+    if (m->pr_host) (void)hipHostFree(m->pr_host);
+    m->pr_dev = m->pr_host = nullptr;
+    m->pr_bytes = 0;
+    if (hipMalloc((void**)&m->pr_dev, bytes) != hipSuccess ||
+        hipHostMalloc((void**)&m->pr_host, bytes, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(KNAPSPEC_ENOMEM, "profiling table allocation failed");
+    }
+    m->pr_bytes = bytes;
+  }
+  if (!m->pr_ev[0]) {
+    if (hipEventCreate(&m->pr_ev[0]) != hipSuccess || hipEventCreate(&m->pr_ev[1]) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(KNAPSPEC_EHIP, "event creation failed");
+    }
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  char* hp = m->pr_host;
+  char* dp = m->pr_dev;
+  *(int32_t*)(hp + o_rowseq) = 0;
+  *(int32_t*)(hp + o_rowstate) = 0;  // state row 0 of sequence 0
+  ((int32_t*)(hp + o_init))[0] = 0;  // budget 0's activation row
+  ((int32_t*)(hp + o_init))[1] = -1;
+  *(const float**)(hp + o_x0) = seq->x0;
+
+  auto upload_tables = [&]() -> int {
+    HIPCHK(hipMemcpyAsync(dp, hp, bytes, hipMemcpyHostToDevice, st));
+    return KNAPSPEC_OK;
+  };
+  auto gemm1 = [&](const void* A, int lda, const void* W, int K, int N, int mode,
+                   int* splits) -> int {
+    ks::GemmArgs g{};
+    g.A = A;
+    g.lda = lda;
+    g.R = 1;
+    g.W = W;
+    g.K = K;
+    g.N = N;
+    g.mode = mode;
+    const ks::GemmPlan p = ks::plan_gemm(m->act, 1, N, K, mode, d.d_ff, m->p_floats);
+    g.ng = p.ng;
+    g.mb = p.mb;
+    g.m_tiles = p.m_tiles;
+    g.n_tiles = p.n_tiles;
+    g.splits = p.splits;
+    g.k_chunk = p.k_chunk;
+    if (mode == ks::GEMM_SWIGLU) {
+      g.H = m->h;
+      g.ldh = d.d_ff;
+      g.ff = d.d_ff;
+    } else {
+      g.P = m->P;
+      g.ldp = N;
+    }
+    *splits = g.splits;
+    HIPCHK(ks::launch_gemm(g, m->act, st));
+    return KNAPSPEC_OK;
+  };
+  auto reduce1 = [&](int splits) -> int {
+    ks::ReduceArgs ra{};
+    ra.P = m->P;
+    ra.splits = splits;
+    ra.R = 1;
+    ra.d = D;
+    ra.state_old = m->state[0];
+    ra.row_state = (const int*)(dp + o_rowstate);
+    ra.E = m->E;
+    HIPCHK(ks::launch_reduce(ra, st));
+    return KNAPSPEC_OK;
+  };
+  auto timed = [&](float* ms, auto&& body) -> int {
+    HIPCHK(hipEventRecord(m->pr_ev[0], st));
+    int rc = body();
+    if (rc) return rc;
+    HIPCHK(hipEventRecord(m->pr_ev[1], st));
+    HIPCHK(hipEventSynchronize(m->pr_ev[1]));
+    HIPCHK(hipEventElapsedTime(ms, m->pr_ev[0], m->pr_ev[1]));
+    return KNAPSPEC_OK;
+  };
+
+  // state row 0 = x0 and its RMSNorm'd activation row (the token entering layer 0)
+  int rc = upload_tables();
+  if (rc) return rc;
+  {
+    ks::InitArgs ia{};
+    ia.n_seqs = 1;
+    ia.Bm = d.max_budgets;
+    ia.d = D;
+    ia.mw = m->mw;
+    ia.x0 = (const float* const*)(dp + o_x0);
+    ia.state = m->state[0];
+    ia.valid = m->valid[0];
+    ia.masks = m->masks[0];
+    ia.rows = (const int*)(dp + o_init);
+    ia.xa = m->xa;
+    ia.act = m->act;
+    ia.eps = d.rms_eps;
+    HIPCHK(ks::launch_init(ia, st));
+  }
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  const int slots = m->n_cus * ks::attention_wgs_per_cu(m->act, dh);
+  std::vector<double> samples(reps);
+  for (int ci = 0; ci < n_ctx; ++ci) {
+    const int ctx = ctx_lens[ci];
+    // tables for this context: RoPE angles, the attention split plan and work list (M = 1)
+    float* rope = (float*)(hp + o_rope);
+    for (int j = 0; j < dh / 2; ++j) {
+      const double ang = (double)ctx * std::pow((double)d.rope_theta, -2.0 * j / (double)dh);
+      rope[j] = (float)std::cos(ang);
+      rope[dh / 2 + j] = (float)std::sin(ang);
+    }
+    std::vector<int> pairs{hkv}, tiles{(ctx + 63) / 64}, nsplit;
+    std::vector<size_t> prow{(size_t)hq};
+    plan_attention_splits(pairs, tiles, prow, slots, ASPLIT_MAX, m->part_slots, nsplit);
+    const int ns = nsplit[0];
+    const int chunk = ns > 0 ? (tiles[0] + ns - 1) / ns * 64 : 64;
+    ks::AttnSeq as{};
+    as.ctx = ctx;
+    as.cap = seq->ctx_capacity;
+    as.row_off = 0;
+    as.M = 1;
+    as.nsplit = ctx > 0 ? (ctx + chunk - 1) / chunk : 0;
+    as.chunk = chunk;
+    as.part_off = 0;
+    int nw = 0;
+    int4* work = (int4*)(hp + o_work);
+    for (int cc = 0; cc < hkv; ++cc)
+      for (int sp = 0; sp < as.nsplit; ++sp) work[nw++] = make_int4(0, cc, 0, sp);
+    for (int r = 0; r < reps; ++r) {
+      const int l = r % d.n_layers;
+      const knapspec_layer_weights& W = m->layers[l];
+      as.k = ctx > 0 ? seq->k_cache[l] : nullptr;
+      as.v = ctx > 0 ? seq->v_cache[l] : nullptr;
+      std::memcpy(hp + o_aseq, &as, sizeof(as));
+      HIPCHK(hipStreamSynchronize(st));  // the pinned tables are rewritten per repetition
+      rc = upload_tables();
+      if (rc) return rc;
+      float ms = 0.f;
+      rc = timed(&ms, [&]() -> int {
+        int splits = 1;
+        int e = gemm1(m->xa, D, W.w_qkv, D, m->nqkv, ks::GEMM_PARTIAL, &splits);
+        if (e) return e;
+        ks::QkvArgs qa{};
+        qa.P = m->P;
+        qa.splits = splits;
+        qa.R = 1;
+        qa.ldp = m->nqkv;
+        qa.hq = hq;
+        qa.hkv = hkv;
+        qa.dh = dh;
+        qa.rope = (const float*)(dp + o_rope);
+        qa.row_seq = (const int*)(dp + o_rowseq);
+        qa.Q = m->q;
+        qa.kself = m->kself;
+        qa.vself = m->vself;
+        HIPCHK(ks::launch_qkv(qa, m->act, st));
+        ks::AttnArgs aa{};
+        aa.Q = m->q;
+        aa.hq = hq;
+        aa.hkv = hkv;
+        aa.dh = dh;
+        aa.work = (const int4*)(dp + o_work);
+        aa.seqs = (const ks::AttnSeq*)(dp + o_aseq);
+        aa.Opart = m->Opart;
+        aa.Mpart = m->Mpart;
+        aa.Lpart = m->Lpart;
+        aa.scale_log2 = scale_log2;
+        HIPCHK(ks::launch_attention(aa, m->act, nw, st));
+        ks::CombineArgs ca{};
+        ca.Q = m->q;
+        ca.kself = m->kself;
+        ca.vself = m->vself;
+        ca.Opart = m->Opart;
+        ca.Mpart = m->Mpart;
+        ca.Lpart = m->Lpart;
+        ca.seqs = (const ks::AttnSeq*)(dp + o_aseq);
+        ca.row_seq = (const int*)(dp + o_rowseq);
+        ca.R = 1;
+        ca.hq = hq;
+        ca.hkv = hkv;
+        ca.dh = dh;
+        ca.scale_log2 = scale_log2;
+        ca.O = m->o;
+        HIPCHK(ks::launch_combine(ca, m->act, st));
+        e = gemm1(m->o, m->qdim, W.w_o, m->qdim, D, ks::GEMM_PARTIAL, &splits);
+        if (e) return e;
+        return reduce1(splits);
+      });
+      if (rc) return rc;
+      samples[r] = 1e3 * ms;
+    }
+    attn_us[ci] = median_of(samples);
+  }
+  for (int r = 0; r < reps; ++r) {
+    const knapspec_layer_weights& W = m->layers[r % d.n_layers];
+    float ms = 0.f;
+    rc = timed(&ms, [&]() -> int {
+      int s1 = 1, splits = 1;
+      int e = gemm1(m->xa, D, W.w_gate_up, D, 2 * d.d_ff, ks::GEMM_SWIGLU, &s1);
+      if (e) return e;
+      e = gemm1(m->h, d.d_ff, W.w_down, d.d_ff, D, ks::GEMM_PARTIAL, &splits);
+      if (e) return e;
+      return reduce1(splits);
+    });
+    if (rc) return rc;
+    samples[r] = 1e3 * ms;
+  }
+  *mlp_us = median_of(samples);
   return KNAPSPEC_OK;
 }

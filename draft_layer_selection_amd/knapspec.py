@@ -90,6 +90,12 @@ SIGNATURES = {
     "knapspec_free_model": (None, [C.c_void_p]),
     "knapspec_last_error": (C.c_char_p, []),
     "knapspec_abi_version": (C.c_int32, []),
+    "knapspec_profile_items": (C.c_int, [C.c_void_p, C.POINTER(knapspec_seq),
+                                         C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.c_void_p,
+                                         C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "knapspec_fit_latency": (C.c_int, [C.POINTER(C.c_int32), C.POINTER(C.c_double), C.c_int32,
+                                       C.POINTER(C.c_double), C.POINTER(C.c_double),
+                                       C.POINTER(C.c_double)]),
 }
 
 if not os.path.exists(LIB_PATH):
@@ -112,6 +118,8 @@ knapspec_mask_words = lib.knapspec_mask_words
 knapspec_free_model = lib.knapspec_free_model
 knapspec_last_error = lib.knapspec_last_error
 knapspec_abi_version = lib.knapspec_abi_version
+knapspec_profile_items = lib.knapspec_profile_items
+knapspec_fit_latency = lib.knapspec_fit_latency
 
 
 class KnapSpecError(RuntimeError):
@@ -159,6 +167,16 @@ def item_weights(n_layers, ctx, n_budgets, attn_base, attn_per_token, mlp, fixed
     _check(knapspec_item_weights(C.byref(lat), n_layers, ctx, n_budgets, _ptr(t, C.c_double),
                                  _ptr(w, C.c_int32)), "knapspec_item_weights")
     return t, w
+
+
+def fit_latency(n, t):
+    """knapspec_fit_latency: least-squares t = a + b*n -> (a, b, r2)."""
+    nn = np.ascontiguousarray(n, dtype=np.int32)
+    tt = np.ascontiguousarray(t, dtype=np.float64)
+    a, b, r2 = C.c_double(), C.c_double(), C.c_double()
+    _check(knapspec_fit_latency(_ptr(nn, C.c_int32), _ptr(tt, C.c_double), len(nn), C.byref(a),
+                                C.byref(b), C.byref(r2)), "knapspec_fit_latency")
+    return a.value, b.value, r2.value
 
 
 class Result:
@@ -212,14 +230,8 @@ class Model:
         _check(knapspec_set_latency_model(self.handle, C.byref(lat)),
                "knapspec_set_latency_model")
 
-    def solve(self, seqs: List[dict], n_budgets: int, gamma, tau: float = -math.inf,
-              max_skip_weight: int = -1, flags: int = 0, stream=None,
-              result: Optional[Result] = None) -> Result:
-        """seqs: dicts with ctx (int), k_cache / v_cache (lists of device tensors per layer,
-        [hkv][capacity][dh]), x0 (device float32 [d])."""
-        torch = self._torch
-        S = len(seqs)
-        carr = (knapspec_seq * S)()
+    def _seq_array(self, seqs: List[dict]):
+        carr = (knapspec_seq * len(seqs))()
         keep = []
         for i, sq in enumerate(seqs):
             kp = (C.c_void_p * self.n_layers)(*[t.data_ptr() for t in sq["k_cache"]])
@@ -228,6 +240,16 @@ class Model:
             cap = int(sq["k_cache"][0].shape[1]) if self.n_layers else 0
             carr[i] = knapspec_seq(int(sq["ctx"]), cap, C.cast(kp, C.POINTER(C.c_void_p)),
                                    C.cast(vp, C.POINTER(C.c_void_p)), sq["x0"].data_ptr())
+        return carr, keep
+
+    def solve(self, seqs: List[dict], n_budgets: int, gamma, tau: float = -math.inf,
+              max_skip_weight: int = -1, flags: int = 0, stream=None,
+              result: Optional[Result] = None) -> Result:
+        """seqs: dicts with ctx (int), k_cache / v_cache (lists of device tensors per layer,
+        [hkv][capacity][dh]), x0 (device float32 [d])."""
+        torch = self._torch
+        S = len(seqs)
+        carr, keep = self._seq_array(seqs)
         s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
         args = knapspec_solve_args(S, carr, int(n_budgets), int(gamma[0]), int(gamma[1]),
                                    float(tau), int(max_skip_weight), int(flags), C.c_void_p(s))
@@ -235,6 +257,20 @@ class Model:
                                                         flags)
         _check(knapspec_solve(self.handle, C.byref(args), C.byref(res.struct)), "knapspec_solve")
         return res
+
+    def profile_items(self, seq: dict, ctx_lens, reps: int = 8, stream=None):
+        """knapspec_profile_items: median microseconds of one token through an Attention item
+        at each context length in ctx_lens, and through an MLP item -> (attn_us, mlp_us)."""
+        torch = self._torch
+        carr, keep = self._seq_array([seq])
+        n = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        attn = np.zeros(len(n), dtype=np.float64)
+        mlp = C.c_double()
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(knapspec_profile_items(self.handle, carr, _ptr(n, C.c_int32), len(n), int(reps),
+                                      C.c_void_p(s), _ptr(attn, C.c_double), C.byref(mlp)),
+               "knapspec_profile_items")
+        return attn, mlp.value
 
     def set_profiling(self, enable: bool):
         _check(knapspec_set_profiling(self.handle, 1 if enable else 0), "knapspec_set_profiling")

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KNAPSPEC_ABI_VERSION 1
+#define KNAPSPEC_ABI_VERSION 2
 
 #define KNAPSPEC_OK 0
 #define KNAPSPEC_EINVAL (-1)       /* bad argument, shape or pointer */
@@ -161,6 +161,29 @@ int knapspec_tpt_select(const float* alpha, const double* t_draft, const uint8_t
  * context length ctx_len (t: 2L doubles, w: 2L int32; either may be NULL).  Needs no GPU. */
 int knapspec_item_weights(const knapspec_latency_model* lat, int32_t n_layers, int32_t ctx_len,
                           int32_t n_budgets, double* t, int32_t* w);
+
+/* Device latency profile of the draft pass's items, the measured item latencies the weights
+ * come from (review, "The reading": an item's weight is its latency, Attention's growing
+ * linearly with the context length and MLP's flat; the paper profiles them once per model).
+ * Times one decode token (M = 1 row) through an Attention item -- q|k|v GEMM, RoPE, attention
+ * over ctx positions of `seq`'s cache plus its own, O GEMM, residual -- at each context length
+ * ctx_lens[0 .. n_ctx-1], and through an MLP item -- gate|up GEMM with SwiGLU, down GEMM,
+ * residual -- each `reps` times, bracketed by HIP events on hip_stream.  Repetition r uses
+ * layer r mod n_layers, so consecutive repetitions stream different weights.
+ * seq: x0 and caches as for knapspec_solve, ctx_capacity >= max(ctx_lens) (ctx_len ignored).
+ * Writes attn_us[n_ctx] and *mlp_us: medians over the repetitions, in microseconds.  Uses the
+ * model's workspace (do not overlap with a solve on the same model).  1 <= n_ctx <= 1024,
+ * 1 <= reps <= 10000; EINVAL for bad arguments, ENOMEM / EHIP for runtime failures. */
+int knapspec_profile_items(knapspec_model* model, const knapspec_seq* seq,
+                           const int32_t* ctx_lens, int32_t n_ctx, int32_t reps,
+                           void* hip_stream, double* attn_us, double* mlp_us);
+
+/* Host-only least-squares line t = a + b*n through (n[i], t[i]), i < count, and its R^2
+ * (1 when every t[i] is equal), e.g. to turn knapspec_profile_items' attention latencies into
+ * the attn_base / attn_per_token of knapspec_latency_model.  Needs count >= 2 points with at
+ * least two distinct n and finite t; EINVAL otherwise. */
+int knapspec_fit_latency(const int32_t* n, const double* t, int32_t count, double* a,
+                         double* b, double* r2);
 
 /* Measurement hook.  With profiling enabled, knapspec_solve brackets every kernel launch with
  * a pair of HIP events on the solve stream and, after its synchronisation, adds the elapsed

@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(ks):
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     out = subprocess.run(["nm", "-D", "--defined-only", ks.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (knapspec_\w+)", out))
@@ -48,7 +48,7 @@ def test_exports_every_declared_symbol(ks):
 
 
 def test_version_and_mask_words(ks):
-    assert ks.knapspec_abi_version() == 1
+    assert ks.knapspec_abi_version() == 2
     assert [ks.knapspec_mask_words(n) for n in (1, 8, 32, 33, 80)] == [1, 1, 1, 2, 3]
 
 
@@ -173,3 +173,41 @@ def test_solve_rejects_null(ks):
     rc = ks.knapspec_solve(None, None, None)
     assert rc == ks.KNAPSPEC_EINVAL
     ks.knapspec_free_model(None)  # no-op
+
+
+def test_fit_latency_matches_least_squares(ks):
+    """The host line fit against numpy's least-squares polynomial fit, on noisy and exact
+    lines, and its R^2 against the definition 1 - RSS/TSS."""
+    rng = np.random.default_rng(5)
+    n = np.array([0, 1024, 4096, 8192, 16384, 32768], dtype=np.int32)
+    for a0, b0, noise in ((10.0, 5e-4, 0.0), (37.7, 5.12e-4, 0.3), (3.1, 0.0, 0.05)):
+        t = a0 + b0 * n + noise * rng.standard_normal(len(n))
+        a, b, r2 = ks.fit_latency(n, t)
+        bb, aa = np.polyfit(n.astype(np.float64), t, 1)
+        assert a == pytest.approx(aa, rel=1e-9, abs=1e-9)
+        assert b == pytest.approx(bb, rel=1e-9, abs=1e-15)
+        resid = t - (aa + bb * n)
+        tss = np.sum((t - t.mean()) ** 2)
+        want = 1.0 - np.sum(resid ** 2) / tss if tss > 0 else 1.0
+        assert r2 == pytest.approx(want, rel=1e-9, abs=1e-12)
+    # exact line: R^2 = 1
+    assert ks.fit_latency([1, 2, 3], [3.0, 5.0, 7.0]) == pytest.approx((1.0, 2.0, 1.0))
+
+
+def test_fit_latency_rejects_bad_input(ks):
+    with pytest.raises(ks.KnapSpecError):
+        ks.fit_latency([5], [1.0])
+    with pytest.raises(ks.KnapSpecError):
+        ks.fit_latency([7, 7, 7], [1.0, 2.0, 3.0])
+    with pytest.raises(ks.KnapSpecError):
+        ks.fit_latency([1, 2], [1.0, float("nan")])
+
+
+def test_profile_items_rejects_null_model(ks):
+    import ctypes as C
+
+    out = (C.c_double * 1)()
+    mlp = C.c_double()
+    n = (C.c_int32 * 1)(0)
+    rc = ks.knapspec_profile_items(None, None, n, 1, 1, None, out, C.byref(mlp))
+    assert rc == ks.KNAPSPEC_EINVAL
