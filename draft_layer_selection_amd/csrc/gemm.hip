@@ -11,7 +11,10 @@
 //     64 banks x 4 B and serves 16-byte reads 16 lanes at a time, so 16 consecutive 128-byte
 //     rows must land on 16 distinct (row parity, slot) pairs for conflict-free MFMA reads;
 //   * the barrier between stages is a bare s_barrier: each wave first waits (vmcnt) for its own
-//     loads of the stage, and a fenced barrier would instead drain every load in flight;
+//     loads of the stage, and a fenced barrier would instead drain every load in flight; every
+//     wave issues the same number of loads per stage and the tail re-issues the last stage, so
+//     the wait count is a compile-time constant and the loop carries no per-stage branches
+//     (branchy per-stage bookkeeping cost ~15-20% at large R, measured);
 //   * activations are re-read from L2 once per column tile, i.e. R/(64*NG) times the weight
 //     bytes, so the planner widens the tile (NG=4) when R > 128;
 //   * K-slice partial sums are reduced through LDS in a fixed order (deterministic); K is split
@@ -177,25 +180,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-// s_waitcnt with vmcnt = n (<= 47) and no wait on the other counters (gfx9 encoding).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-#define KS_WAITVM(N)                                                                        \
-  case N:                                                                                   \
-    __builtin_amdgcn_s_waitcnt(((N)&15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14));       \
-    break;
-    KS_WAITVM(0) KS_WAITVM(1) KS_WAITVM(2) KS_WAITVM(3) KS_WAITVM(4) KS_WAITVM(5)
-    KS_WAITVM(6) KS_WAITVM(7) KS_WAITVM(8) KS_WAITVM(9) KS_WAITVM(10) KS_WAITVM(11)
-    KS_WAITVM(12) KS_WAITVM(13) KS_WAITVM(14) KS_WAITVM(15) KS_WAITVM(16) KS_WAITVM(17)
-    KS_WAITVM(18) KS_WAITVM(19) KS_WAITVM(20) KS_WAITVM(21) KS_WAITVM(22) KS_WAITVM(23)
-    KS_WAITVM(24) KS_WAITVM(25) KS_WAITVM(26) KS_WAITVM(27) KS_WAITVM(28) KS_WAITVM(29)
-    KS_WAITVM(30) KS_WAITVM(31) KS_WAITVM(32) KS_WAITVM(33) KS_WAITVM(34) KS_WAITVM(35)
-    KS_WAITVM(36) KS_WAITVM(37) KS_WAITVM(38) KS_WAITVM(39) KS_WAITVM(40)
-#undef KS_WAITVM
-    default:
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-      break;
-  }
+// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_const() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 template <int NG, int MB, int S>
@@ -232,16 +221,18 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
 
   // Loader: chunk q = 8 stage rows; lane -> row 8q + lane/8, LDS slot lane%8 which holds the
   // row's global 16-byte chunk (lane%8) ^ ((row >> 1) % 8).
+  // Every wave issues PER_WAVE chunks per stage; a wave past the last chunk repeats an earlier
+  // chunk into that chunk's own place (same bytes), so the per-stage load count is the same
+  // for all waves and the waits below are compile-time constants.
   const bf16* src[PER_WAVE];
   const int rin = lane >> 3;
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
-    const int q = wave + 8 * j;
+    int q = wave + 8 * j;
+    q = q < NCH ? q : q - NCH;
     const int r = 8 * q + rin;
     const int cglob = (lane & 7) ^ ((r >> 1) & 7);
-    if (q >= NCH) {
-      src[j] = W;
-    } else if (r < WR) {
+    if (r < WR) {
       int wrow;
       if (a.mode == GEMM_SWIGLU)
         wrow = r < WR / 2 ? nt * (WR / 2) + r : a.ff + nt * (WR / 2) + (r - WR / 2);
@@ -254,14 +245,14 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
       src[j] = A + (size_t)ar * a.lda + k0 + 8 * cglob;
     }
   }
-  const int my_loads = (NCH - wave + 7) / 8;  // chunks this wave issues per stage
+  static_assert(8 * PER_WAVE - NCH <= NCH, "at most one repeat per chunk");
   auto issue = [&](int stage, int slot) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int q = wave + 8 * j;
-      if (q < NCH)
-        __builtin_amdgcn_global_load_lds((const void*)(src[j] + stage * 64),
-                                         (void*)(smem + slot * STAGE + q * 1024), 16, 0, 0);
+      int q = wave + 8 * j;
+      q = q < NCH ? q : q - NCH;
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + stage * 64),
+                                       (void*)(smem + slot * STAGE + q * 1024), 16, 0, 0);
     }
   };
 
@@ -273,17 +264,18 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
       acc[mb][0][r] = 0.f;
       acc[mb][1][r] = 0.f;
     }
+  // Stages past the last one are clamped to it: the repeated loads land in slots that no
+  // later stage reads, and every stage issues the same number of loads.
 #pragma unroll
-  for (int p = 0; p < S - 1; ++p)
-    if (p < nit) issue(p, p);
+  for (int p = 0; p < S - 1; ++p) issue(min(p, nit - 1), p);
 
   // one 64-K stage; slot J is a compile-time constant (the loop below is unrolled by S), so
   // the LDS addresses are per-lane registers plus immediates
   auto stage = [&](auto Jc, int it) {
     constexpr int J = decltype(Jc)::value;
-    wait_vmcnt(min(S - 2, nit - 1 - it) * my_loads);  // this wave's part of stage `it` landed
-    asm volatile("s_barrier" ::: "memory");            // ... and everyone else's
-    if (it + S - 1 < nit) issue(it + S - 1, (J + S - 1) % S);  // refill the slot freed above
+    wait_vm_const<(S - 2) * PER_WAVE>();  // this wave's part of stage `it` landed
+    asm volatile("s_barrier" ::: "memory");  // ... and everyone else's
+    issue(min(it + S - 1, nit - 1), (J + S - 1) % S);  // refill the slot freed above
     const unsigned char* st = smem + J * STAGE;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -306,12 +298,16 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
       }
     }
   };
-  for (int it = 0; it < nit; it += S) {
-    static_for<S>([&](auto Jc) {
-      constexpr int J = decltype(Jc)::value;
-      if (it + J < nit) stage(Jc, it + J);
-    });
-  }
+  // whole rounds of S stages without conditions (the compiler then tracks the outstanding
+  // loads exactly), then the remainder
+  int it0 = 0;
+  for (; it0 + S <= nit; it0 += S)
+    static_for<S>([&](auto Jc) { stage(Jc, it0 + decltype(Jc)::value); });
+  static_for<S>([&](auto Jc) {
+    constexpr int J = decltype(Jc)::value;
+    if (it0 + J < nit) stage(Jc, it0 + J);
+  });
+  wait_vm_const<0>();  // repeated tail loads may still be writing the ring the reduction reuses
   __syncthreads();
 
   float (*red)[32][RP] = (float (*)[32][RP])smem;

@@ -19,6 +19,8 @@ namespace ks {
 namespace {
 
 constexpr int SEL_THREADS = 256;
+constexpr int SELR_THREADS = 512;  // register-resident select: up to SELR_MAXIT float4 per row
+constexpr int SELR_MAXIT = 4;
 
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   const int d4 = a.d / 4;
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   *(f32x4*)(a.E + off) = res + v;
 }
 
-template <int N>
+template <int N, int THREADS = SEL_THREADS>
 __device__ __forceinline__ void block_sum(float (&v)[N], float* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -46,7 +48,7 @@ __device__ __forceinline__ void block_sum(float (&v)[N], float* scratch) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     float t = scratch[i];
-    for (int w = 1; w < SEL_THREADS / 64; ++w) t += scratch[w * N + i];
+    for (int w = 1; w < THREADS / 64; ++w) t += scratch[w * N + i];
     v[i] = t;
   }
   __syncthreads();
@@ -174,6 +176,115 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   }
 }
 
+// The same select with the rows held in registers between the two passes (one global read of
+// each row instead of two) and 512 threads per budget: for d <= 4 * 4 * SELR_THREADS.
+// Sums are taken in the same per-thread order as select_kernel would with 512 threads; the
+// decision and the written rows are those of the definition above.
+template <class T, int IT>
+__global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) {
+  const int q = blockIdx.x / (a.B + 1);
+  const int b = blockIdx.x % (a.B + 1);
+  const bool is_ref = b == a.B;
+  const ItemSeq inf = a.info[q];
+  const int d4 = a.d / 4;
+  const size_t sstride = (size_t)(a.Bm + 1) * a.d;
+  const float* st_old = a.state_old + q * sstride;
+  float* st_new = a.state_new + q * sstride;
+  const float* ref = a.E + (size_t)inf.ref_row * a.d;
+  __shared__ float scratch[8 * (SELR_THREADS / 64)];
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  if (is_ref) {
+    f32x4 r[IT];
+    float ss[1] = {0.f};
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int e4 = threadIdx.x + i * SELR_THREADS;
+      r[i] = e4 < d4 ? *(const f32x4*)(ref + 4 * e4) : zero;
+      if (e4 < d4) *(f32x4*)(st_new + (size_t)a.Bm * a.d + 4 * e4) = r[i];
+      ss[0] += r[i][0] * r[i][0] + r[i][1] * r[i][1] + r[i][2] * r[i][2] + r[i][3] * r[i][3];
+    }
+    if (inf.next_ref_row < 0) return;
+    block_sum<1, SELR_THREADS>(ss, scratch);
+    const float scale = 1.0f / sqrtf(ss[0] / (float)a.d + a.eps);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int e4 = threadIdx.x + i * SELR_THREADS;
+      if (e4 < d4) store_act<T>(a.xa_next, inf.next_ref_row, a.d, e4, r[i], scale);
+    }
+    return;
+  }
+
+  const int qb = q * a.Bm + b;
+  const int erow = a.exec_row[qb];
+  const int src = b - inf.w;
+  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
+  const bool has_skip = a.valid_old[qb] != 0;
+  const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;
+  const float* g_row = st_old + (size_t)b * a.d;
+
+  f32x4 ev[IT], gv[IT];
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e4 = threadIdx.x + i * SELR_THREADS;
+    const bool in = e4 < d4;
+    const f32x4 r = (in && (has_exec || has_skip)) ? *(const f32x4*)(ref + 4 * e4) : zero;
+    ev[i] = (in && has_exec) ? *(const f32x4*)(e_row + 4 * e4) : zero;
+    gv[i] = (in && has_skip) ? *(const f32x4*)(g_row + 4 * e4) : zero;
+    acc[0] += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
+    acc[1] += ev[i][0] * r[0] + ev[i][1] * r[1] + ev[i][2] * r[2] + ev[i][3] * r[3];
+    acc[2] += ev[i][0] * ev[i][0] + ev[i][1] * ev[i][1] + ev[i][2] * ev[i][2] + ev[i][3] * ev[i][3];
+    acc[3] += gv[i][0] * r[0] + gv[i][1] * r[1] + gv[i][2] * r[2] + gv[i][3] * r[3];
+    acc[4] += gv[i][0] * gv[i][0] + gv[i][1] * gv[i][1] + gv[i][2] * gv[i][2] + gv[i][3] * gv[i][3];
+  }
+  block_sum<5, SELR_THREADS>(acc, scratch);
+  const float c_e = has_exec ? nan_to_ninf(acc[1] / (sqrtf(acc[2]) * sqrtf(acc[0]))) : -INFINITY;
+  const float c_s = has_skip ? nan_to_ninf(acc[3] / (sqrtf(acc[4]) * sqrtf(acc[0]))) : -INFINITY;
+  const bool take = c_e > c_s;
+  const float best = take ? c_e : c_s;
+  bool alive = best > -INFINITY;
+  if (best < a.tau) alive = false;
+  if (a.skip_cap >= 0 && inf.prefix - b > a.skip_cap) alive = false;
+
+  if (threadIdx.x == 0) {
+    a.valid_new[qb] = alive ? 1 : 0;
+    const size_t cell = ((size_t)q * a.n_items + a.item) * a.Bm + b;
+    if (a.decisions) a.decisions[cell] = alive ? (take ? 1 : 0) : 255;
+    if (a.margins) {
+      const bool he = c_e > -INFINITY, hs = c_s > -INFINITY;
+      a.margins[cell] = (he && hs) ? fabsf(c_e - c_s) : ((he != hs) ? INFINITY : NAN);
+    }
+    if (a.item == a.n_items - 1) a.cos_out[qb] = alive ? best : NAN;
+  }
+  if (threadIdx.x < a.mw) {
+    const int wd = threadIdx.x;
+    uint64_t mval = 0;
+    if (alive) {
+      if (take) {
+        mval = a.mask_old[((size_t)q * a.Bm + src) * a.mw + wd];
+        if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
+      } else {
+        mval = a.mask_old[(size_t)qb * a.mw + wd];
+      }
+    }
+    a.mask_new[(size_t)qb * a.mw + wd] = mval;
+  }
+
+  const int nrow = a.next_row[qb];
+  const float ms = (take ? acc[2] : acc[4]) / (float)a.d;
+  const float scale = alive ? 1.0f / sqrtf(ms + a.eps) : 0.f;
+  float* out = st_new + (size_t)b * a.d;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e4 = threadIdx.x + i * SELR_THREADS;
+    if (e4 >= d4) continue;
+    const f32x4 x = alive ? (take ? ev[i] : gv[i]) : zero;
+    if (alive) *(f32x4*)(out + 4 * e4) = x;
+    if (nrow >= 0) store_act<T>(a.xa_next, nrow, a.d, e4, x, scale);
+  }
+}
+
 // DP start: budget 0 and the reference hold x0; every other budget is empty.
 template <class T>
 __global__ __launch_bounds__(SEL_THREADS) void init_kernel(InitArgs a) {
@@ -211,12 +322,25 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_seqs * (a.B + 1)), block(SEL_THREADS);
-  if (a.act == ACT_F32)
-    hipLaunchKernelGGL(select_kernel<float>, grid, block, 0, s, a);
+template <class T>
+static void launch_select_t(const SelectArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_seqs * (a.B + 1));
+  const int it = (a.d / 4 + SELR_THREADS - 1) / SELR_THREADS;
+  if (it <= 1)
+    hipLaunchKernelGGL((select_reg_kernel<T, 1>), grid, dim3(SELR_THREADS), 0, s, a);
+  else if (it <= 2)
+    hipLaunchKernelGGL((select_reg_kernel<T, 2>), grid, dim3(SELR_THREADS), 0, s, a);
+  else if (it <= SELR_MAXIT)
+    hipLaunchKernelGGL((select_reg_kernel<T, SELR_MAXIT>), grid, dim3(SELR_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(select_kernel<bf16>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(select_kernel<T>, grid, dim3(SEL_THREADS), 0, s, a);
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  if (a.act == ACT_F32)
+    launch_select_t<float>(a, s);
+  else
+    launch_select_t<bf16>(a, s);
   return hipGetLastError();
 }
 
