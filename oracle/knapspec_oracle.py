@@ -26,6 +26,12 @@ Pins (tests that tie this code to something other than itself):
                                 linear-in-context attention latency.
   * Lemma 4.1                   cosine-margin => same greedy token, on DP states and on
                                 constructed pairs at the bound.
+  * window (r > 1) attention    processing r tokens as one causal block equals decoding them
+                                one at a time with each token's key/value appended to the
+                                cache; a token never depends on later window tokens;
+                                loop-based attention on tiny inputs.
+  * alpha_lm_head               the full-model state scores 1; planted LM heads with known
+                                greedy tokens; values on the grid {0, 1/r, ..., 1}.
 Parity unpinned: the full DP at the Qwen3-1.7B, Llama-3-8B and Llama-3-70B shapes has no
 independent check beyond the pins above and the per-mask self-consistency of the results.
 """
@@ -164,6 +170,57 @@ def attention_item(X: np.ndarray, w_qkv: np.ndarray, w_o: np.ndarray, k_cache: n
     return (X + o.reshape(M, hq * dh) @ w_o.T).astype(F32)
 
 
+def attention_item_window(X: np.ndarray, w_qkv: np.ndarray, w_o: np.ndarray,
+                          k_cache: np.ndarray, v_cache: np.ndarray, ctx: int,
+                          s: DecoderShape) -> np.ndarray:
+    """One Attention item applied to r-token states X [M][r][d].
+
+    Review, referee major comment 4: the DP table holds r x d hidden states per cell, r being
+    the tokens of the recent-token cache (window m, free parameters).  Reading taken here:
+    the r tokens of a state enter the item together as the newest positions ctx .. ctx+r-1
+    (token t at position ctx + t); every token attends to the cached positions 0..ctx-1 and,
+    causally, to the keys/values that the item computes for tokens 0..t of the same state.
+    With r = 1 this is attention_item.
+    """
+    M, r, d = X.shape
+    hq, hkv, dh = s.n_q_heads, s.n_kv_heads, s.head_dim
+    G = hq // hkv
+    xn = rmsnorm(X, s.rms_eps)
+    qkv = xn @ w_qkv.T
+    q = qkv[:, :, : hq * dh].reshape(M, r, hq, dh)
+    k = qkv[:, :, hq * dh:(hq + hkv) * dh].reshape(M, r, hkv, dh)
+    v = qkv[:, :, (hq + hkv) * dh:].reshape(M, r, hkv, dh)
+    for t in range(r):
+        cos, sin = rope_cos_sin(ctx + t, dh, s.rope_theta)
+        q[:, t] = rope(q[:, t], cos, sin)
+        k[:, t] = rope(k[:, t], cos, sin)
+    scale = F32(1.0 / np.sqrt(dh))
+    causal = np.tril(np.ones((r, r), dtype=bool))          # [t][t'] key t' visible to t
+    o = np.empty((M, r, hq, dh), dtype=F32)
+    for c in range(hkv):
+        Q = q[:, :, c * G:(c + 1) * G, :]                    # [M][r][G][dh]
+        Kw, Vw = k[:, :, c, :], v[:, :, c, :]                # [M][r'][dh]
+        sw = np.einsum("mtgd,mud->mtgu", Q, Kw).astype(F32) * scale
+        sw = np.where(causal[None, :, None, :], sw, -np.inf).astype(F32)
+        mx = sw.max(axis=3)
+        if ctx > 0:
+            Kc = widen(k_cache[c, :ctx, :])
+            Vc = widen(v_cache[c, :ctx, :])
+            sc = (Q.reshape(M * r * G, dh) @ Kc.T).reshape(M, r, G, ctx) * scale
+            mx = np.maximum(mx, sc.max(axis=3))
+            pc = np.exp(sc - mx[..., None])
+            num = (pc.reshape(-1, ctx) @ Vc).reshape(M, r, G, dh)
+            den = pc.sum(axis=3, dtype=F32)
+        else:
+            num = np.zeros((M, r, G, dh), dtype=F32)
+            den = np.zeros((M, r, G), dtype=F32)
+        pw = np.exp(sw - mx[..., None]).astype(F32)           # masked keys give exp(-inf) = 0
+        num = num + np.einsum("mtgu,mud->mtgd", pw, Vw).astype(F32)
+        den = den + pw.sum(axis=3, dtype=F32)
+        o[:, :, c * G:(c + 1) * G, :] = num / den[..., None]
+    return (X + o.reshape(M, r, hq * dh) @ w_o.T).astype(F32)
+
+
 def mlp_item(X: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
              s: DecoderShape) -> np.ndarray:
     """One MLP item: X + (silu(xn W_g^T) * (xn W_u^T)) W_d^T, rows independent."""
@@ -195,11 +252,18 @@ class DecoderItems:
         return w
 
     def __call__(self, i: int, X: np.ndarray) -> np.ndarray:
+        """X: [M][d] single-token states, or [M][r][d] r-token states (window)."""
         layer = i // 2
         w = self._weights(layer)
         if i % 2 == 0:
             kc, vc = self.kv[layer]
+            if X.ndim == 3:
+                return attention_item_window(X, w["w_qkv"], w["w_o"], kc, vc, self.ctx, self.s)
             return attention_item(X, w["w_qkv"], w["w_o"], kc, vc, self.ctx, self.s)
+        if X.ndim == 3:
+            M, r, d = X.shape
+            return mlp_item(X.reshape(M * r, d), w["w_gate_up"], w["w_down"],
+                            self.s).reshape(M, r, d)
         return mlp_item(X, w["w_gate_up"], w["w_down"], self.s)
 
 
@@ -208,9 +272,14 @@ class DecoderItems:
 # --------------------------------------------------------------------------------------
 
 def cos_rows(A: np.ndarray, r: np.ndarray) -> np.ndarray:
-    """Cosine of each row of A with vector r, in float64; 0/0 gives NaN."""
-    A64 = A.astype(F64)
-    r64 = r.astype(F64)
+    """Cosine of each state A[m] with the state r, in float64; 0/0 gives NaN.
+
+    An r-token state [r][d] is compared as the flattened r*d vector (the Frobenius inner
+    product of the two matrices over the product of their Frobenius norms) -- the reading
+    taken for the cosine of the paper's r x d states.
+    """
+    A64 = A.astype(F64).reshape(A.shape[0], -1)
+    r64 = r.astype(F64).reshape(-1)
     with np.errstate(invalid="ignore", divide="ignore"):
         return (A64 @ r64) / (np.sqrt(np.sum(A64 * A64, axis=1)) * np.sqrt(r64 @ r64))
 
@@ -222,8 +291,8 @@ class DPResult:
     cos: np.ndarray         # float64 [B], NaN where invalid
     decisions: np.ndarray   # uint8 [n_items][B]: 0 skip, 1 execute, 255 invalid
     margins: np.ndarray     # float64 [n_items][B]: |c_e - c_s|, inf if one option, NaN if none
-    states: np.ndarray      # float32 [B][d] final candidate states
-    ref: np.ndarray         # float32 [d] full-model state after the last item
+    states: np.ndarray      # float32 [B][d] (or [B][r][d]) final candidate states
+    ref: np.ndarray         # float32 [d] (or [r][d]) full-model state after the last item
 
 
 def knapsack_dp(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: int,
@@ -252,9 +321,8 @@ def knapsack_dp(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: in
         exceeds it (the review's editorial reading of a K/2 skip cap).
     """
     B = int(n_budgets)
-    x0 = np.asarray(x0, dtype=F32)
-    d = x0.shape[0]
-    g = np.zeros((B, d), dtype=F32)
+    x0 = np.asarray(x0, dtype=F32)           # [d], or [r][d] for r-token states
+    g = np.zeros((B,) + x0.shape, dtype=F32)
     valid = np.zeros(B, dtype=bool)
     bits = np.zeros((B, n_items), dtype=bool)
     g[0] = x0
@@ -269,7 +337,7 @@ def knapsack_dp(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: in
         wi = int(w[i])
         prefix += wi
         src = np.nonzero(valid[: max(0, B - wi)])[0]
-        rows = np.concatenate([g[src], ref[None, :]], axis=0)
+        rows = np.concatenate([g[src], ref[None]], axis=0)
         out = apply_item(i, rows)
         ex, ref_new = out[:-1], out[-1].astype(F32)
         tgt = src + wi
@@ -297,7 +365,7 @@ def knapsack_dp(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: in
 
         new_g = g.copy()
         new_bits = bits.copy()
-        e_full = np.zeros((B, d), dtype=F32)
+        e_full = np.zeros_like(g)
         e_full[tgt] = ex
         tb = np.nonzero(take)[0]
         new_g[tb] = e_full[tb]
@@ -338,7 +406,7 @@ def eval_subsets(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: i
     """cos(f^(S)(x0), f(x0)) at the last depth for each subset row of ``bits`` [R][n_items]."""
     R = bits.shape[0]
     x0 = np.asarray(x0, dtype=F32)
-    rows = np.repeat(x0[None, :], R + 1, axis=0)
+    rows = np.repeat(x0[None], R + 1, axis=0)
     for i in range(n_items):
         sel = np.concatenate([np.nonzero(bits[:, i])[0], [R]])
         rows[sel] = apply_item(i, rows[sel])
@@ -352,7 +420,7 @@ def brute_force(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: in
     Subset id bit i = item i executed.  Review, "What would settle it": enumerate all layer
     subsets of a small model and compare with the DP's per-budget choice.
     """
-    rows = np.asarray(x0, dtype=F32)[None, :].copy()
+    rows = np.asarray(x0, dtype=F32)[None].copy()
     ids = np.zeros(1, dtype=np.int64)
     for i in range(n_items):
         ex = apply_item(i, rows)
@@ -413,6 +481,41 @@ def alpha_from_cos(cos: np.ndarray) -> np.ndarray:
     return a
 
 
+def greedy_tokens(X: np.ndarray, w_lm: np.ndarray, eps: float):
+    """Greedy next token of each token state: argmax_v (rmsnorm(x) . w_lm[v]) in float64,
+    ties to the smaller v.  X [..., d], w_lm [V][d] (float32 or bf16 bits).  Returns
+    (tokens [...], margin between the two largest logits [...])."""
+    W = widen(w_lm).astype(F64)
+    x = rmsnorm(np.asarray(X, dtype=F32), eps).astype(F64)
+    logits = x.reshape(-1, x.shape[-1]) @ W.T
+    tok = np.argmax(logits, axis=1)
+    top2 = np.sort(logits, axis=1)[:, -2:] if W.shape[0] > 1 else np.stack(
+        [np.full(len(tok), -np.inf), logits[:, 0]], axis=1)
+    return tok.reshape(x.shape[:-1]), (top2[:, 1] - top2[:, 0]).reshape(x.shape[:-1])
+
+
+def alpha_lm_head(states: np.ndarray, valid: np.ndarray, ref: np.ndarray, w_lm: np.ndarray,
+                  eps: float) -> np.ndarray:
+    """History estimate of the acceptance rate for every budget: the fraction of the r window
+    tokens whose greedy token under the candidate's final state equals the full model's.
+
+    Review, free parameters (cache window m "used for DP and acceptance estimation") and the
+    circularity check (Eq. 9: a history-based estimate of alpha_S); the formula is not printed.
+    Reading: compare greedy tokens through an LM head with the RMSNorm'd final states, the
+    full model's tokens standing in for the accepted history.  0 where a budget is invalid.
+    """
+    states = np.asarray(states, dtype=F32)
+    B = states.shape[0]
+    if states.ndim == 2:
+        states = states[:, None, :]
+        ref = np.asarray(ref)[None, :]
+    r = states.shape[1]
+    tok, _ = greedy_tokens(states, w_lm, eps)
+    tref, _ = greedy_tokens(ref, w_lm, eps)
+    a = (tok == tref[None, :]).sum(axis=1).astype(F64) / r
+    return np.where(np.asarray(valid, dtype=bool), a, 0.0)
+
+
 # --------------------------------------------------------------------------------------
 # One full solve
 # --------------------------------------------------------------------------------------
@@ -428,17 +531,20 @@ class SolveResult:
     best_budget: int
     best_gamma: int
     best_tpt: float
+    alpha: np.ndarray = None  # float64 [B] acceptance estimate the TPT grid used
 
 
 def solve(shape: DecoderShape, layers, kv, x0: np.ndarray, ctx: int, latency: dict,
           n_budgets: int, gamma: Sequence[int], tau: float = -np.inf, skip_cap: int = -1,
           per_item: Optional[Sequence[float]] = None, cache_widened: bool = False,
-          apply_item: Optional[Callable] = None) -> SolveResult:
+          apply_item: Optional[Callable] = None,
+          w_lm: Optional[np.ndarray] = None) -> SolveResult:
     """Latencies -> weights -> DP -> per-budget draft latency -> TPT grid, for one sequence.
 
     t_Draft(S) = fixed + sum_{i in S} t_i and t_Target = fixed + sum_i t_i: one draft pass
     runs the kept items, one verification pass runs all of them (readings; the page defines
-    TPT in terms of both but prints no formula for them).
+    TPT in terms of both but prints no formula for them).  x0 is [d] (one token) or [r][d]
+    (an r-token window).  With ``w_lm`` the TPT grid uses alpha_lm_head, else clamp(cos).
     """
     n_items = 2 * shape.n_layers
     t = item_latencies(shape.n_layers, ctx, latency["attn_base"], latency["attn_per_token"],
@@ -450,7 +556,11 @@ def solve(shape: DecoderShape, layers, kv, x0: np.ndarray, ctx: int, latency: di
     fixed = float(latency.get("fixed", 0.0))
     t_draft = np.array([fixed + float(np.sum(t[dp.bits[b]])) for b in range(n_budgets)])
     t_target = fixed + float(np.sum(t))
-    alpha = alpha_from_cos(dp.cos)
+    if w_lm is not None:
+        alpha = alpha_lm_head(dp.states, dp.valid, dp.ref, w_lm, shape.rms_eps)
+    else:
+        alpha = alpha_from_cos(dp.cos)
     bb, bg, bt = tpt_select(alpha, t_draft, dp.valid, t_target, int(gamma[0]), int(gamma[1]))
     return SolveResult(dp=dp, t=t, w=w, masks=pack_masks(dp.bits), t_draft=t_draft,
-                       t_target=t_target, best_budget=bb, best_gamma=bg, best_tpt=bt)
+                       t_target=t_target, best_budget=bb, best_gamma=bg, best_tpt=bt,
+                       alpha=alpha)

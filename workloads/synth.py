@@ -10,8 +10,10 @@ Distributions (no values are printed on the pages; these are the recipe of this 
   weights   N(0, 0.02^2)   row-major [out][in]: w_qkv [(hq+2hkv)*dh][d] (q|k|v blocks),
                            w_o [d][hq*dh], w_gate_up [2*ff][d] (gate|up blocks), w_down [d][ff]
   KV cache  N(0, 1)        [hkv][ctx][dh] per layer, treated as already position-rotated keys
-  x0        N(0, 0.02^2)   the current token's input hidden state, [d]
-  LM head   N(0, 0.02^2)   [vocab][d] (used only by the cosine-margin lemma check)
+  x0        N(0, 0.02^2)   the current token's input hidden state, [d]; for an r-token
+                           window, [r][d] (token t of the window drawn under its own key)
+  LM head   N(0, 0.02^2)   [vocab][d] (the cosine-margin lemma check and the acceptance
+                           estimate over a window)
 
 This module is shared by the GPU path's harness and by the CPU oracle's tests.  It holds
 no part of the method's arithmetic: only random draws, dtype rounding and bookkeeping.
@@ -27,7 +29,7 @@ import numpy as np
 
 from .configs import Workload
 
-T_WQKV, T_WO, T_WGU, T_WDOWN, T_KCACHE, T_VCACHE, T_X0, T_CTX, T_LMHEAD = range(9)
+T_WQKV, T_WO, T_WGU, T_WDOWN, T_KCACHE, T_VCACHE, T_X0, T_CTX, T_LMHEAD, T_X0WIN = range(10)
 CHUNK = 1 << 22
 
 W_SIGMA = 0.02
@@ -116,9 +118,22 @@ def x0(wl: Workload, seq: int = 0, resolve: int = 0, seed: int = 0) -> np.ndarra
     return bf16_bits_to_f32(v) if s.dtype == "bf16" else v
 
 
-def lm_head(wl: Workload, vocab: int = 4096, seed: int = 0) -> np.ndarray:
+def x0_window(wl: Workload, r: int, seq: int = 0, resolve: int = 0, seed: int = 0) -> np.ndarray:
+    """Input states [r][d] of an r-token window (model dtype, widened to float32).  r = 1
+    gives x0() as a [1][d] array."""
+    if r == 1:
+        return x0(wl, seq, resolve, seed)[None, :]
+    s = wl.shape
+    v = normal((r, s.d_model), X0_SIGMA, s.dtype, [seed, wl.cfg_id, T_X0WIN, resolve, seq])
+    return bf16_bits_to_f32(v) if s.dtype == "bf16" else v
+
+
+def lm_head(wl: Workload, vocab: int = 4096, seed: int = 0, bits: bool = False) -> np.ndarray:
+    """LM head [vocab][d]; model dtype widened to float32, or the raw bf16 bit patterns."""
     s = wl.shape
     v = normal((vocab, s.d_model), W_SIGMA, s.dtype, [seed, wl.cfg_id, T_LMHEAD, 0, 0])
+    if bits:
+        return v
     return bf16_bits_to_f32(v) if s.dtype == "bf16" else v
 
 
