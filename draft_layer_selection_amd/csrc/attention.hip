@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void qkv_kernel(QkvArgs a) {
   const int lane = threadIdx.x & 63;
   const int r = widx / heads, hd = widx % heads;
   const int half = a.dh / 2;
-  const float* rope = a.rope + (size_t)a.row_seq[r] * a.dh;
+  const float* rope = a.rope + ((size_t)a.row_seq[r] * a.wmax + a.row_tok[r]) * a.dh;
   for (int j = lane; j < half; j += 64) {
     const size_t base = (size_t)r * a.ldp + (size_t)hd * a.dh;
     float x0 = a.P[base + j];
@@ -472,12 +472,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const AttnSeq S = a.seqs[a.row_seq[r]];
   const int e0 = lane * EPL;
   const T* q = (const T*)a.Q + ((size_t)r * a.hq + h) * DH + e0;
-  const float* ks = a.kself + ((size_t)r * a.hkv + c) * DH + e0;
-  const float* vs = a.vself + ((size_t)r * a.hkv + c) * DH + e0;
-  float d = 0.f;
+  // window keys: the own keys of the rows of window tokens 0..tw of this state (tw = 0: the
+  // row's own key only)
+  const int tw = a.row_tok[r];
+  float s_w[WIN_MAX];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) d = fmaf(to_f32(q[e]), ks[e], d);
-  const float s_self = warp_sum(d) * a.scale_log2;
+  for (int k = 0; k < WIN_MAX; ++k) {
+    s_w[k] = -INFINITY;
+    if (k <= tw) {
+      const float* ks = a.kself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(to_f32(q[e]), ks[e], d);
+      s_w[k] = warp_sum(d) * a.scale_log2;
+    }
+  }
   const size_t qrow = (size_t)r * a.hq + h;
   const int rl = r - S.row_off;
   const size_t slot0 = attn_slot(S, 0, rl, a.hq, h);
@@ -487,14 +496,33 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const bool has = lane < ns;
   const float ms = has ? a.Mpart[slot0 + lane * split_stride] : -INFINITY;
   const float ls = has ? a.Lpart[slot0 + lane * split_stride] : 0.f;
-  const float mx = fmaxf(warp_max(ms), s_self);
+  float mx = fmaxf(warp_max(ms), s_w[0]);
+#pragma unroll
+  for (int k = 1; k < WIN_MAX; ++k)
+    if (k <= tw) mx = fmaxf(mx, s_w[k]);
   const float wsp = has ? exp2f(ms - mx) : 0.f;
-  const float w_self = exp2f(s_self - mx);
-  const float den = warp_sum(wsp * ls) + w_self;
+  float w_w[WIN_MAX];
+#pragma unroll
+  for (int k = 0; k < WIN_MAX; ++k) w_w[k] = k <= tw ? exp2f(s_w[k] - mx) : 0.f;
+  float den = warp_sum(wsp * ls) + w_w[0];
+#pragma unroll
+  for (int k = 1; k < WIN_MAX; ++k)
+    if (k <= tw) den += w_w[k];
   const float inv = 1.0f / den;
   float num[EPL];
+  {
+    const float* vs = a.vself + ((size_t)(r - tw) * a.hkv + c) * DH + e0;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) num[e] = w_self * vs[e];
+    for (int e = 0; e < EPL; ++e) num[e] = w_w[0] * vs[e];
+  }
+#pragma unroll
+  for (int k = 1; k < WIN_MAX; ++k) {
+    if (k <= tw) {
+      const float* vs = a.vself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) num[e] = fmaf(w_w[k], vs[e], num[e]);
+    }
+  }
   // splits in groups of 8 with the loads of a group issued together (fixed summation order)
   const float* op = a.Opart + slot0 * DH + e0;
   for (int sp0 = 0; sp0 < ns; sp0 += 8) {

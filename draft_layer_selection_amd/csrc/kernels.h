@@ -17,6 +17,8 @@ enum ActType : int { ACT_F32 = 0, ACT_BF16 = 1 };
 // ---------------------------------------------------------------------------------------
 enum GemmMode : int { GEMM_PARTIAL = 0, GEMM_SWIGLU = 1 };
 
+constexpr int WIN_MAX = 8;  // largest window r (tokens per DP state)
+
 struct GemmArgs {
   const void* A;  // [R][lda] activations (bf16 or f32, same as W)
   int lda;
@@ -81,8 +83,10 @@ struct AttnArgs {
 
 struct CombineArgs {
   const void* Q;
-  const float* kself;  // [R][hkv][dh]
+  const float* kself;  // [R][hkv][dh]: the item's own keys/values of every row
   const float* vself;
+  const int* row_tok;  // [R] window token t of the row: it also attends to the own
+                       // keys/values of rows r - t .. r (window tokens 0..t of its state)
   const float* Opart;
   const float* Mpart;
   const float* Lpart;
@@ -97,8 +101,10 @@ struct QkvArgs {
   const float* P;      // [splits][R][ldp]
   int splits, R, ldp;
   int hq, hkv, dh;
-  const float* rope;   // [n_seqs][dh] : cos[dh/2] then sin[dh/2]
+  const float* rope;   // [n_seqs][wmax][dh]: cos[dh/2] then sin[dh/2] at position ctx + t
   const int* row_seq;  // [R]
+  const int* row_tok;  // [R] window token t of the row
+  int wmax;
   void* Q;             // [R][hq][dh] activations
   float* kself;        // [R][hkv][dh]
   float* vself;
@@ -111,10 +117,11 @@ struct ItemSeq {   // one (item, sequence)
   int w;           // item weight
   int prefix;      // w_0 + ... + w_i
   int row_off;     // first row of the sequence in this item
-  int M;           // rows (sources + reference)
-  int ref_row;     // global row of the reference in this item's GEMM output
-  int next_ref_row;// global row of the reference in the next item's activations (-1: last)
-  int pad0, pad1;
+  int M;           // rows ((sources + reference) x window)
+  int ref_row;     // global row of the reference's first token in this item's GEMM output
+  int next_ref_row;// same in the next item's activations (-1: none)
+  int win;         // r: tokens per state (rows per budget)
+  int pad1;
 };
 
 // E[r] = state_old[row_state[r]] + sum_s P[s][r]: the item applied to every source row and
@@ -129,16 +136,18 @@ struct ReduceArgs {
 
 struct SelectArgs {
   int item, n_items, B, Bm, d, mw, n_seqs;
+  int wmax;                // state rows per budget slot (window capacity)
+  int rmax;                // largest window r among the solve's sequences
   const float* E;          // [Rtot][d] item outputs incl. residual (ReduceArgs::E)
   int Rtot;
-  const float* state_old;  // [S][Bm+1][d], index Bm = reference
+  const float* state_old;  // [S][Bm+1][wmax][d], budget index Bm = reference
   float* state_new;
   const uint8_t* valid_old;  // [S][Bm]
   uint8_t* valid_new;
   const uint64_t* mask_old;  // [S][Bm][mw]
   uint64_t* mask_new;
-  const int* exec_row;     // [S][Bm] row of this item whose target budget is b, or -1
-  const int* next_row;     // [S][Bm] row of b in the next item's activations, or -1
+  const int* exec_row;     // [S][Bm] first row of this item whose target budget is b, or -1
+  const int* next_row;     // [S][Bm] first row of b in the next item's activations, or -1
   const ItemSeq* info;     // [S]
   float tau;
   int skip_cap;
@@ -151,18 +160,31 @@ struct SelectArgs {
 };
 
 struct InitArgs {
-  int n_seqs, Bm, d, mw;
-  const float* const* x0;  // device array [n_seqs] of device pointers
-  float* state;            // [S][Bm+1][d]
+  int n_seqs, Bm, d, mw, wmax;
+  const float* const* x0;  // device array [n_seqs] of device pointers to [r][d]
+  float* state;            // [S][Bm+1][wmax][d]
   uint8_t* valid;          // [S][Bm]
   uint64_t* masks;         // [S][Bm][mw]
-  const int* rows;         // [S][2]: row of budget 0 and of the reference in item 0 (-1 none)
+  const int* rows;         // [S][4]: first row of budget 0 and of the reference in item 0
+                           // (-1 none), the window r, unused
   void* xa;                // item 0 activations
   int act;
   float eps;
 };
 
+// Running greedy token of each row over vocabulary chunks: logits of columns
+// col0 .. col0+ncols-1 are the K-split partial sums P[s][row][c] (added in split order);
+// the best (value, index) replaces the row's running best only when strictly larger, ties
+// within a chunk go to the lower index, and NaN logits never win.
+struct LmArgmaxArgs {
+  const float* P;   // [splits][R][ldp]
+  int splits, R, ldp, ncols, col0, first;
+  float* best_val;  // [R]
+  int* best_idx;    // [R]
+};
+
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
+hipError_t launch_lm_argmax(const LmArgmaxArgs& a, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);

@@ -59,25 +59,27 @@ struct Carver {
 // Byte offsets of the per-solve map / launch tables (same layout on host and device).  The
 // attention work lists come last so that a solve uploads only the part it filled.
 struct MapLayout {
-  size_t exec, next, rowseq, rowstate, info, work, aseq, rope, x0, init, total, max_work;
+  size_t exec, next, rowseq, rowstate, rowtok, info, work, aseq, rope, x0, init, total,
+      max_work;
 };
 
 MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int hkv, int G,
-                     int dh, int asplit_max) {
+                     int dh, int asplit_max, size_t wmax) {
   MapLayout L{};
   Carver c;
   L.exec = c.take((size_t)L2 * S * Bm * 4);
   L.next = c.take((size_t)L2 * S * Bm * 4);
   L.rowseq = c.take((size_t)L2 * Rmax * 4);
   L.rowstate = c.take((size_t)L2 * Rmax * 4);
+  L.rowtok = c.take((size_t)L2 * Rmax * 4);
   L.info = c.take((size_t)L2 * S * sizeof(ks::ItemSeq));
   L.aseq = c.take((size_t)n_layers * S * sizeof(ks::AttnSeq));
-  L.rope = c.take(S * dh * 4);
+  L.rope = c.take(S * wmax * dh * 4);
   L.x0 = c.take(S * 8);
-  L.init = c.take(S * 2 * 4);
+  L.init = c.take(S * 4 * 4);
   // per layer: every (sequence, KV head, query block, split) once, plus the empty entries
   // that keep each die's share of the list aligned (at most one query-block group per die)
-  const size_t qb_max = (G * (Bm + 1) + 63) / 64;
+  const size_t qb_max = (G * (Bm + 1) * wmax + 63) / 64;
   L.max_work = (size_t)n_layers * (S * hkv * qb_max * asplit_max + N_XCD * qb_max);
   L.work = c.take(L.max_work * 16);
   L.total = c.off;
@@ -145,6 +147,7 @@ struct knapspec_model {
 
   // dimensions
   int L2 = 0, mw = 0, qdim = 0, kvdim = 0, nqkv = 0, Rmax = 0;
+  int wmax = 1;  // tokens per state slot (largest window)
   size_t p_floats = 0;
   size_t part_slots = 0;  // attention partial results: (split, row, query head) slots
   int n_cus = 0;
@@ -192,6 +195,12 @@ struct knapspec_model {
   char* h_out = nullptr;
   size_t h_out_bytes = 0;
 
+  // LM head of the acceptance estimate (knapspec_set_lm_head); running argmax per row
+  const void* lm_w = nullptr;
+  int lm_vocab = 0;
+  float* lm_val = nullptr;
+  int* lm_idx = nullptr;
+
   // item latency profiling (knapspec_profile_items): small tables, allocated on first use
   char* pr_dev = nullptr;
   char* pr_host = nullptr;
@@ -202,6 +211,8 @@ struct knapspec_model {
     for (hipEvent_t e : pr_ev)
       if (e) (void)hipEventDestroy(e);
     if (pr_dev) (void)hipFree(pr_dev);
+    if (lm_val) (void)hipFree(lm_val);
+    if (lm_idx) (void)hipFree(lm_idx);
     if (pr_host) (void)hipHostFree(pr_host);
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
     if (gexec) (void)hipGraphExecDestroy(gexec);
@@ -363,6 +374,8 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
     return fail(KNAPSPEC_EINVAL, "max_budgets must be in [2, %d]", MAX_BUDGETS);
   if (d.max_seqs < 1) return fail(KNAPSPEC_EINVAL, "max_seqs must be >= 1");
   if (d.max_ctx < 0) return fail(KNAPSPEC_EINVAL, "max_ctx must be >= 0");
+  if (d.max_window < 0 || d.max_window > KNAPSPEC_WINDOW_MAX)
+    return fail(KNAPSPEC_EINVAL, "max_window must be in [0, %d]", KNAPSPEC_WINDOW_MAX);
   if (!(d.rms_eps > 0.f) || !std::isfinite(d.rms_eps))
     return fail(KNAPSPEC_EINVAL, "rms_eps must be finite and > 0");
   if (!(d.rope_theta > 0.f) || !std::isfinite(d.rope_theta))
@@ -416,13 +429,17 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   m->kvdim = d.n_kv_heads * d.head_dim;
   m->nqkv = m->qdim + 2 * m->kvdim;
   const size_t S = d.max_seqs, Bm = d.max_budgets, D = d.d_model;
-  m->Rmax = (int)(S * Bm);
+  m->wmax = std::max(1, (int)d.max_window);
+  const size_t Wm = m->wmax;
+  // rows of one item: per sequence (live sources + reference) x window; the acceptance
+  // estimate's LM-head pass uses (budgets + reference) x window rows
+  m->Rmax = (int)(S * (Bm + 1) * Wm);
   const size_t R = m->Rmax;
   const size_t nmax = std::max<size_t>(m->nqkv, D);
   m->p_floats = std::max<size_t>(PSPLIT_MAX * std::min<size_t>(R, 256), R) * nmax;
 
   Carver c;
-  const size_t o_state = c.take(2 * S * (Bm + 1) * D * 4);
+  const size_t o_state = c.take(2 * S * (Bm + 1) * Wm * D * 4);
   const size_t o_valid = c.take(2 * S * Bm);
   const size_t o_masks = c.take(2 * S * Bm * m->mw * 8);
   const size_t o_xa = c.take(R * D * m->elem);
@@ -443,7 +460,7 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   // row maps and launch tables, rebuilt on the host each solve and uploaded once
   const int G = d.n_q_heads / d.n_kv_heads;
   m->maps_bytes = map_layout(m->L2, d.n_layers, S, Bm, R, d.n_kv_heads, G, d.head_dim,
-                             ASPLIT_MAX).total;
+                             ASPLIT_MAX, Wm).total;
   const size_t o_maps = c.take(m->maps_bytes);
   m->ws_bytes = c.off;
 
@@ -455,7 +472,8 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
     return fail(KNAPSPEC_ENOMEM, "device workspace allocation of %zu bytes failed", need);
   }
   m->h_out_bytes = align_up(S * Bm * m->mw * 8) + align_up(S * Bm * 4) + align_up(S * Bm) +
-                   align_up(S * m->L2 * Bm) + align_up(S * m->L2 * Bm * 4);
+                   align_up(S * m->L2 * Bm) + align_up(S * m->L2 * Bm * 4) +
+                   align_up(S * (Bm + 1) * Wm * 4);
   if (hipHostMalloc((void**)&m->h_maps, m->maps_bytes, hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&m->h_out, m->h_out_bytes, hipHostMallocDefault) != hipSuccess) {
     (void)hipGetLastError();
@@ -470,7 +488,7 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   }
   char* ws = m->ws;
   m->state[0] = (float*)(ws + o_state);
-  m->state[1] = m->state[0] + S * (Bm + 1) * D;
+  m->state[1] = m->state[0] + S * (Bm + 1) * Wm * D;
   m->valid[0] = (uint8_t*)(ws + o_valid);
   m->valid[1] = m->valid[0] + S * Bm;
   m->masks[0] = (uint64_t*)(ws + o_masks);
@@ -512,6 +530,27 @@ KS_API int knapspec_set_latency_model(knapspec_model* m, const knapspec_latency_
     if (!(total > 0.0)) return fail(KNAPSPEC_EINVAL, "per_item latencies sum to zero");
   }
   m->have_latency = true;
+  return KNAPSPEC_OK;
+}
+
+KS_API int knapspec_set_lm_head(knapspec_model* m, const void* w, int32_t vocab) {
+  if (!m) return fail(KNAPSPEC_EINVAL, "model is NULL");
+  if (!w) return fail(KNAPSPEC_EINVAL, "LM head pointer is NULL");
+  if (vocab < 1 || vocab > (1 << 24)) return fail(KNAPSPEC_EINVAL, "vocab must be in [1, 2^24]");
+  if (m->act == ks::ACT_BF16 && vocab % 64)
+    return fail(KNAPSPEC_EUNSUPPORTED, "bf16 kernels need vocab % 64 == 0");
+  if (!m->lm_val) {
+    if (hipMalloc((void**)&m->lm_val, (size_t)m->Rmax * 4) != hipSuccess ||
+        hipMalloc((void**)&m->lm_idx, (size_t)m->Rmax * 4) != hipSuccess) {
+      (void)hipGetLastError();
+      if (m->lm_val) (void)hipFree(m->lm_val);
+      m->lm_val = nullptr;
+      m->lm_idx = nullptr;
+      return fail(KNAPSPEC_ENOMEM, "LM-head argmax buffers allocation failed");
+    }
+  }
+  m->lm_w = w;
+  m->lm_vocab = vocab;
   return KNAPSPEC_OK;
 }
 
@@ -605,6 +644,9 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     return fail(KNAPSPEC_EINVAL, "KNAPSPEC_RETURN_DECISIONS set but result.decisions is NULL");
   if ((args->flags & KNAPSPEC_RETURN_MARGINS) && !res->margins)
     return fail(KNAPSPEC_EINVAL, "KNAPSPEC_RETURN_MARGINS set but result.margins is NULL");
+  const bool use_lm = (args->flags & KNAPSPEC_ALPHA_LM_HEAD) != 0;
+  if (use_lm && !m->lm_w)
+    return fail(KNAPSPEC_EINVAL, "KNAPSPEC_ALPHA_LM_HEAD set but no LM head (knapspec_set_lm_head)");
   for (int q = 0; q < S; ++q) {
     const knapspec_seq& sq = args->seqs[q];
     if (sq.ctx_len < 0 || sq.ctx_len > d.max_ctx)
@@ -612,6 +654,9 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     if (sq.ctx_capacity < sq.ctx_len)
       return fail(KNAPSPEC_EINVAL, "seq %d: ctx_capacity < ctx_len", q);
     if (!sq.x0) return fail(KNAPSPEC_EINVAL, "seq %d: x0 is NULL", q);
+    if (sq.window < 0 || std::max(1, (int)sq.window) > m->wmax)
+      return fail(KNAPSPEC_EINVAL, "seq %d: window must be in [0, %d] (model max_window)", q,
+                  m->wmax);
     if (sq.ctx_len > 0) {
       if (!sq.k_cache || !sq.v_cache) return fail(KNAPSPEC_EINVAL, "seq %d: cache arrays NULL", q);
       for (int l = 0; l < d.n_layers; ++l)
@@ -625,6 +670,16 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
 
   const int L2 = m->L2, Bm = d.max_budgets, D = d.d_model, mw = m->mw;
   const int hq = d.n_q_heads, hkv = d.n_kv_heads, dh = d.head_dim, G = hq / hkv;
+  const int Wm = m->wmax;
+  // window r of each sequence; rows of its LM-head pass start at lm_off[q]
+  std::vector<int> win(S), lm_off(S);
+  int rmax = 1, Rlm = 0;
+  for (int q = 0; q < S; ++q) {
+    win[q] = std::max(1, (int)args->seqs[q].window);
+    rmax = std::max(rmax, win[q]);
+    lm_off[q] = Rlm;
+    Rlm += (B + 1) * win[q];
+  }
 
   // ---- per-sequence weights and budget reachability (data independent when tau is off;
   //      the kernels re-check validity on the device, so pruning only removes work).
@@ -649,22 +704,22 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       for (int s : p.src[i]) reach[s + w] = 1;
     }
   }
-  // rows of each item: per sequence [sources..., reference]
+  // rows of each item: per sequence [sources..., reference], each a group of r token rows
   std::vector<int> Rtot(L2, 0);
   std::vector<int> row_off((size_t)L2 * S);
   for (int i = 0; i < L2; ++i) {
     int r = 0;
     for (int q = 0; q < S; ++q) {
       row_off[(size_t)i * S + q] = r;
-      r += (int)plan[q].src[i].size() + 1;
+      r += ((int)plan[q].src[i].size() + 1) * win[q];
     }
     Rtot[i] = r;
   }
 
   // ---- build the map/launch tables in pinned host memory
-  const MapLayout ml = map_layout(L2, d.n_layers, S, Bm, m->Rmax, hkv, G, dh, ASPLIT_MAX);
+  const MapLayout ml = map_layout(L2, d.n_layers, S, Bm, m->Rmax, hkv, G, dh, ASPLIT_MAX, Wm);
   const size_t o_exec = ml.exec, o_next = ml.next, o_rowseq = ml.rowseq,
-               o_rowstate = ml.rowstate, o_info = ml.info,
+               o_rowstate = ml.rowstate, o_rowtok = ml.rowtok, o_info = ml.info,
                o_work = ml.work, o_aseq = ml.aseq, o_rope = ml.rope, o_x0 = ml.x0,
                o_init = ml.init, max_work = ml.max_work;
   const size_t qb_rows = ks::attention_qblock(m->act, dh);
@@ -674,6 +729,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   int32_t* next_row = (int32_t*)(hm + o_next);
   int32_t* row_seq = (int32_t*)(hm + o_rowseq);
   int32_t* row_state = (int32_t*)(hm + o_rowstate);
+  int32_t* row_tok = (int32_t*)(hm + o_rowtok);
   ks::ItemSeq* info = (ks::ItemSeq*)(hm + o_info);
   int4* work = (int4*)(hm + o_work);
   ks::AttnSeq* aseq = (ks::AttnSeq*)(hm + o_aseq);
@@ -687,29 +743,38 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     for (int q = 0; q < S; ++q) {
       const SeqPlan& p = plan[q];
       const int off = row_off[(size_t)i * S + q];
-      const int M = (int)p.src[i].size() + 1;
-      for (int r = 0; r < M; ++r) {
-        row_seq[(size_t)i * m->Rmax + off + r] = q;
-        // state row the item is applied to: source budget, or the reference (index Bm)
-        row_state[(size_t)i * m->Rmax + off + r] =
-            q * (Bm + 1) + (r + 1 < M ? p.src[i][r] : Bm);
-      }
+      const int ng = (int)p.src[i].size() + 1;  // groups: sources, then the reference
+      const int wr = win[q];
+      for (int j = 0; j < ng; ++j)
+        for (int t = 0; t < wr; ++t) {
+          const size_t row = (size_t)i * m->Rmax + off + (size_t)j * wr + t;
+          row_seq[row] = q;
+          // state row the item is applied to: token t of a source budget or of the reference
+          // (budget index Bm) in the [S][Bm+1][wmax] slot layout
+          row_state[row] = (q * (Bm + 1) + (j + 1 < ng ? p.src[i][j] : Bm)) * Wm + t;
+          row_tok[row] = t;
+        }
       int32_t* er = exec_row + ((size_t)i * S + q) * Bm;
-      for (int r = 0; r + 1 < M; ++r) er[p.src[i][r] + p.w[i]] = off + r;
+      for (int j = 0; j + 1 < ng; ++j) er[p.src[i][j] + p.w[i]] = off + j * wr;
       ks::ItemSeq& in = info[(size_t)i * S + q];
       in.w = p.w[i];
       in.prefix = p.prefix[i];
       in.row_off = off;
-      in.M = M;
-      in.ref_row = off + M - 1;
+      in.M = ng * wr;
+      in.ref_row = off + (ng - 1) * wr;
       in.next_ref_row = -1;
-      in.pad0 = in.pad1 = 0;
+      in.win = wr;
+      in.pad1 = 0;
+      int32_t* nr = next_row + ((size_t)i * S + q) * Bm;
       if (i + 1 < L2) {
         const int noff = row_off[(size_t)(i + 1) * S + q];
-        const int nM = (int)p.src[i + 1].size() + 1;
-        int32_t* nr = next_row + ((size_t)i * S + q) * Bm;
-        for (int r = 0; r + 1 < nM; ++r) nr[p.src[i + 1][r]] = noff + r;
-        in.next_ref_row = noff + nM - 1;
+        const int nng = (int)p.src[i + 1].size() + 1;
+        for (int j = 0; j + 1 < nng; ++j) nr[p.src[i + 1][j]] = noff + j * wr;
+        in.next_ref_row = noff + (nng - 1) * wr;
+      } else if (use_lm) {
+        // the final states' RMSNorm'd rows feed the LM-head pass: budget b, then the reference
+        for (int b = 0; b < B; ++b) nr[b] = lm_off[q] + b * wr;
+        in.next_ref_row = lm_off[q] + B * wr;
       }
     }
   }
@@ -727,7 +792,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     for (int l = 0; l < d.n_layers; ++l) {
       const int i = 2 * l;
       for (int q = 0; q < S; ++q) {
-        const int M = (int)plan[q].src[i].size() + 1;
+        const int M = ((int)plan[q].src[i].size() + 1) * win[q];
         qblocks[q] = (int)((G * M + qb_rows - 1) / qb_rows);
         pairs[q] = hkv * qblocks[q];
         tiles[q] = (args->seqs[q].ctx_len + 63) / 64;
@@ -739,7 +804,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       std::vector<size_t> load(N_XCD, 0);
       for (int q = 0; q < S; ++q) {
         const knapspec_seq& sq = args->seqs[q];
-        const int M = (int)plan[q].src[i].size() + 1;
+        const int M = ((int)plan[q].src[i].size() + 1) * win[q];
         const int ctx = sq.ctx_len;
         const int ns = nsplit[q];
         const int chunk = ns > 0 ? (tiles[q] + ns - 1) / ns * 64 : 64;
@@ -753,7 +818,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
         as.nsplit = ctx > 0 ? (ctx + chunk - 1) / chunk : 0;
         as.chunk = chunk;
         as.part_off = (int)part;
-        as.pad0 = as.pad1 = as.pad2 = 0;
+        as.pad0 = win[q];
+        as.pad1 = as.pad2 = 0;
         part += (size_t)as.nsplit * M * hq;
         for (int c = 0; c < hkv; ++c)
           for (int sp = 0; sp < as.nsplit; ++sp) {
@@ -776,17 +842,23 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       work_cnt[l] = (int)nw - work_off[l];
     }
   }
-  // RoPE table at position ctx_len of each sequence: angle_j = n * theta^(-2j/dh) in float64
+  // RoPE tables at positions ctx_len + t of each sequence's window tokens:
+  // angle_j = n * theta^(-2j/dh) in float64
   for (int q = 0; q < S; ++q) {
-    const double n = (double)args->seqs[q].ctx_len;
-    for (int j = 0; j < dh / 2; ++j) {
-      const double ang = n * std::pow((double)d.rope_theta, -2.0 * j / (double)dh);
-      rope[(size_t)q * dh + j] = (float)std::cos(ang);
-      rope[(size_t)q * dh + dh / 2 + j] = (float)std::sin(ang);
+    for (int t = 0; t < Wm; ++t) {
+      const double n = (double)args->seqs[q].ctx_len + t;
+      float* rt = rope + ((size_t)q * Wm + t) * dh;
+      for (int j = 0; j < dh / 2; ++j) {
+        const double ang = n * std::pow((double)d.rope_theta, -2.0 * j / (double)dh);
+        rt[j] = (float)std::cos(ang);
+        rt[dh / 2 + j] = (float)std::sin(ang);
+      }
     }
     x0p[q] = args->seqs[q].x0;
-    init_rows[2 * q] = plan[q].src[0].empty() ? -1 : row_off[q];
-    init_rows[2 * q + 1] = row_off[q] + (int)plan[q].src[0].size();
+    init_rows[4 * q] = plan[q].src[0].empty() ? -1 : row_off[q];
+    init_rows[4 * q + 1] = row_off[q] + (int)plan[q].src[0].size() * win[q];
+    init_rows[4 * q + 2] = win[q];
+    init_rows[4 * q + 3] = 0;
   }
 
   // ---- output staging layout (pinned host)
@@ -797,6 +869,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   const size_t ho_valid = oc.take((size_t)S * Bm);
   const size_t ho_dec = oc.take((size_t)S * L2 * Bm);
   const size_t ho_mar = oc.take((size_t)S * L2 * Bm * 4);
+  const size_t ho_tok = oc.take((size_t)S * (Bm + 1) * Wm * 4);
   const bool want_dec = (args->flags & KNAPSPEC_RETURN_DECISIONS) != 0;
   const bool want_mar = (args->flags & KNAPSPEC_RETURN_MARGINS) != 0;
 
@@ -808,6 +881,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   const int32_t* d_next = (const int32_t*)(dm + o_next);
   const int32_t* d_rowseq = (const int32_t*)(dm + o_rowseq);
   const int32_t* d_rowstate = (const int32_t*)(dm + o_rowstate);
+  const int32_t* d_rowtok = (const int32_t*)(dm + o_rowtok);
   const ks::ItemSeq* d_info = (const ks::ItemSeq*)(dm + o_info);
   const int4* d_work = (const int4*)(dm + o_work);
   const ks::AttnSeq* d_aseq = (const ks::AttnSeq*)(dm + o_aseq);
@@ -821,6 +895,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     ia.Bm = Bm;
     ia.d = D;
     ia.mw = mw;
+    ia.wmax = Wm;
     ia.x0 = (const float* const*)(dm + o_x0);
     ia.state = m->state[0];
     ia.valid = m->valid[0];
@@ -886,6 +961,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       qa.dh = dh;
       qa.rope = d_rope;
       qa.row_seq = d_rowseq + (size_t)i * m->Rmax;
+      qa.row_tok = d_rowtok + (size_t)i * m->Rmax;
+      qa.wmax = Wm;
       qa.Q = m->q;
       qa.kself = m->kself;
       qa.vself = m->vself;
@@ -910,6 +987,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       ca.Q = m->q;
       ca.kself = m->kself;
       ca.vself = m->vself;
+      ca.row_tok = d_rowtok + (size_t)i * m->Rmax;
       ca.Opart = m->Opart;
       ca.Mpart = m->Mpart;
       ca.Lpart = m->Lpart;
@@ -954,6 +1032,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     sa.d = D;
     sa.mw = mw;
     sa.n_seqs = S;
+    sa.wmax = Wm;
+    sa.rmax = rmax;
     sa.E = m->E;
     sa.Rtot = R;
     sa.state_old = m->state[cur];
@@ -977,6 +1057,34 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     HIPCHK(ks::launch_select(sa, st));
     prof_end(m, pks, st);
     cur ^= 1;
+  }
+
+  // ---- LM-head pass: greedy token of every window token of every budget's final state and
+  //      of the reference, over vocabulary chunks that fit the partial-output buffer
+  if (use_lm) {
+    const size_t per_chunk = m->p_floats / (size_t)std::max(1, Rlm);
+    const int vc = (int)std::min<size_t>((size_t)m->lm_vocab, std::max<size_t>(64, per_chunk / 256 * 256));
+    for (int v0 = 0; v0 < m->lm_vocab; v0 += vc) {
+      const int nc = std::min(vc, m->lm_vocab - v0);
+      int sp = 1;
+      const void* wchunk = (const char*)m->lm_w + (size_t)v0 * D * m->elem;
+      int rc = gemm(m->xa, D, Rlm, wchunk, D, nc, ks::GEMM_PARTIAL, &sp, KNAPSPEC_K_LM_HEAD);
+      if (rc) return rc;
+      ks::LmArgmaxArgs la{};
+      la.P = m->P;
+      la.splits = sp;
+      la.R = Rlm;
+      la.ldp = nc;
+      la.ncols = nc;
+      la.col0 = v0;
+      la.first = v0 == 0;
+      la.best_val = m->lm_val;
+      la.best_idx = m->lm_idx;
+      const int pk = prof_begin(m, KNAPSPEC_K_LM_HEAD, st);
+      HIPCHK(ks::launch_lm_argmax(la, st));
+      prof_end(m, pk, st);
+    }
+    HIPCHK(hipMemcpyAsync(ho + ho_tok, m->lm_idx, (size_t)Rlm * 4, hipMemcpyDeviceToHost, st));
   }
 
   // ---- results back to the host
@@ -1010,8 +1118,10 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     int32_t tau_bits;
     std::memcpy(&tau_bits, &args->tau, 4);
     key.insert(key.end(), {S, B, tau_bits, args->max_skip_weight, args->flags});
+    if (use_lm) key.insert(key.end(), {(int64_t)(intptr_t)m->lm_w, m->lm_vocab});
     for (int q = 0; q < S; ++q) {
       key.push_back(args->seqs[q].ctx_len);
+      key.push_back(win[q]);
       for (int i = 0; i < L2; ++i) key.push_back(plan[q].w[i]);
     }
     hipStream_t own = m->own_stream;
@@ -1071,9 +1181,33 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     double t_target = fixed;
     for (int i = 0; i < L2; ++i) t_target += p.t[i];
     if (!(t_target > 0.0)) return fail(KNAPSPEC_EINVAL, "target pass latency must be > 0");
-    tpt_grid(res->cos + (size_t)q * B, res->t_draft + (size_t)q * B, res->valid + (size_t)q * B, B,
-             t_target, args->gamma_min, args->gamma_max, res->best_budget + q,
-             res->best_gamma + q, res->best_tpt + q);
+    // acceptance estimate per budget: clamp(cos, 0, 1), or the LM-head match fraction
+    std::vector<float> alpha(B, 0.f);
+    const int wr = win[q];
+    const int32_t* ht = (const int32_t*)(ho + ho_tok) + lm_off[q];
+    for (int b = 0; b < B; ++b) {
+      const size_t dst = (size_t)q * B + b;
+      if (!res->valid[dst]) continue;
+      if (use_lm) {
+        int match = 0;
+        for (int t = 0; t < wr; ++t) match += ht[b * wr + t] == ht[B * wr + t];
+        alpha[b] = (float)match / (float)wr;
+      } else {
+        const float c = res->cos[dst];
+        alpha[b] = c == c ? std::min(1.f, std::max(0.f, c)) : 0.f;
+      }
+    }
+    if (res->alpha) std::memcpy(res->alpha + (size_t)q * B, alpha.data(), (size_t)B * 4);
+    if (res->tokens) {
+      int32_t* to = res->tokens + (size_t)lm_off[q];
+      for (int b = 0; b <= B; ++b)
+        for (int t = 0; t < wr; ++t)
+          to[b * wr + t] = !use_lm ? -1
+                           : (b < B && !res->valid[(size_t)q * B + b]) ? -1 : ht[b * wr + t];
+    }
+    tpt_grid(alpha.data(), res->t_draft + (size_t)q * B, res->valid + (size_t)q * B, B, t_target,
+             args->gamma_min, args->gamma_max, res->best_budget + q, res->best_gamma + q,
+             res->best_tpt + q);
     if (want_dec) {
       const uint8_t* hd = (const uint8_t*)(ho + ho_dec);
       for (int i = 0; i < L2; ++i)
@@ -1160,13 +1294,14 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
     return fail(KNAPSPEC_EINVAL, "current HIP device differs from the model's device");
 
   const int hq = d.n_q_heads, hkv = d.n_kv_heads, dh = d.head_dim, D = d.d_model;
-  // table layout: rope [dh] f32 | row_seq, row_state [1] i32 | init rows [2] | x0 ptr |
-  // AttnSeq | work list
+  // table layout: rope [dh] f32 | row_seq, row_state, row_tok [1] i32 | init rows [4] |
+  // x0 ptr | AttnSeq | work list
   Carver c;
   const size_t o_rope = c.take(dh * 4);
   const size_t o_rowseq = c.take(4);
   const size_t o_rowstate = c.take(4);
-  const size_t o_init = c.take(8);
+  const size_t o_rowtok = c.take(4);
+  const size_t o_init = c.take(16);
   const size_t o_x0 = c.take(8);
   const size_t o_aseq = c.take(sizeof(ks::AttnSeq));
   const size_t max_work = (size_t)hkv * ASPLIT_MAX;
@@ -1195,8 +1330,11 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
   char* dp = m->pr_dev;
   *(int32_t*)(hp + o_rowseq) = 0;
   *(int32_t*)(hp + o_rowstate) = 0;  // state row 0 of sequence 0
+  *(int32_t*)(hp + o_rowtok) = 0;    // one token (window r = 1)
   ((int32_t*)(hp + o_init))[0] = 0;  // budget 0's activation row
   ((int32_t*)(hp + o_init))[1] = -1;
+  ((int32_t*)(hp + o_init))[2] = 1;
+  ((int32_t*)(hp + o_init))[3] = 0;
   *(const float**)(hp + o_x0) = seq->x0;
 
   auto upload_tables = [&]() -> int {
@@ -1263,6 +1401,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
     ia.Bm = d.max_budgets;
     ia.d = D;
     ia.mw = m->mw;
+    ia.wmax = m->wmax;
     ia.x0 = (const float* const*)(dp + o_x0);
     ia.state = m->state[0];
     ia.valid = m->valid[0];
@@ -1326,6 +1465,8 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
         qa.dh = dh;
         qa.rope = (const float*)(dp + o_rope);
         qa.row_seq = (const int*)(dp + o_rowseq);
+        qa.row_tok = (const int*)(dp + o_rowtok);
+        qa.wmax = 1;
         qa.Q = m->q;
         qa.kself = m->kself;
         qa.vself = m->vself;
@@ -1351,6 +1492,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
         ca.Lpart = m->Lpart;
         ca.seqs = (const ks::AttnSeq*)(dp + o_aseq);
         ca.row_seq = (const int*)(dp + o_rowseq);
+        ca.row_tok = (const int*)(dp + o_rowtok);
         ca.R = 1;
         ca.hq = hq;
         ca.hkv = hkv;

@@ -73,7 +73,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   const bool is_ref = b == a.B;
   const ItemSeq inf = a.info[q];
   const int d4 = a.d / 4;
-  const size_t sstride = (size_t)(a.Bm + 1) * a.d;  // per-sequence state stride
+  const size_t slot = (size_t)a.wmax * a.d;  // floats per budget slot (token 0 used)
+  const size_t sstride = (size_t)(a.Bm + 1) * slot;  // per-sequence state stride
   const float* st_old = a.state_old + q * sstride;
   float* st_new = a.state_new + q * sstride;
   const float* ref = a.E + (size_t)inf.ref_row * a.d;
@@ -83,14 +84,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
     float ss[1] = {0.f};
     for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
       const f32x4 r = *(const f32x4*)(ref + 4 * e4);
-      *(f32x4*)(st_new + (size_t)a.Bm * a.d + 4 * e4) = r;
+      *(f32x4*)(st_new + (size_t)a.Bm * slot + 4 * e4) = r;
       ss[0] += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
     }
     if (inf.next_ref_row < 0) return;
     block_sum<1>(ss, scratch);
     const float scale = 1.0f / sqrtf(ss[0] / (float)a.d + a.eps);
     for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
-      const f32x4 r = *(const f32x4*)(st_new + (size_t)a.Bm * a.d + 4 * e4);
+      const f32x4 r = *(const f32x4*)(st_new + (size_t)a.Bm * slot + 4 * e4);
       store_act<T>(a.xa_next, inf.next_ref_row, a.d, e4, r, scale);
     }
     return;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
   const bool has_skip = a.valid_old[qb] != 0;
   const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;
-  const float* g_row = st_old + (size_t)b * a.d;
+  const float* g_row = st_old + (size_t)b * slot;
 
   // pass 1: rr, er, ee, gr, gg
   float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   }
   const float ms = (take ? acc[2] : acc[4]) / (float)a.d;
   const float scale = 1.0f / sqrtf(ms + a.eps);
-  float* out = st_new + (size_t)b * a.d;
+  float* out = st_new + (size_t)b * slot;
   for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
     const f32x4 x = take ? *(const f32x4*)(e_row + 4 * e4) : *(const f32x4*)(g_row + 4 * e4);
     *(f32x4*)(out + 4 * e4) = x;
@@ -177,7 +178,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
 }
 
 // The same select with the rows held in registers between the two passes (one global read of
-// each row instead of two) and 512 threads per budget: for d <= 4 * 4 * SELR_THREADS.
+// each row instead of two) and 512 threads per budget: for d <= 4 * 4 * SELR_THREADS and
+// single-token states (window r = 1; a budget's state is token 0 of its wmax-row slot).
 // Sums are taken in the same per-thread order as select_kernel would with 512 threads; the
 // decision and the written rows are those of the definition above.
 template <class T, int IT>
@@ -187,7 +189,8 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   const bool is_ref = b == a.B;
   const ItemSeq inf = a.info[q];
   const int d4 = a.d / 4;
-  const size_t sstride = (size_t)(a.Bm + 1) * a.d;
+  const size_t slot = (size_t)a.wmax * a.d;  // floats per budget slot
+  const size_t sstride = (size_t)(a.Bm + 1) * slot;
   const float* st_old = a.state_old + q * sstride;
   float* st_new = a.state_new + q * sstride;
   const float* ref = a.E + (size_t)inf.ref_row * a.d;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
     for (int i = 0; i < IT; ++i) {
       const int e4 = threadIdx.x + i * SELR_THREADS;
       r[i] = e4 < d4 ? *(const f32x4*)(ref + 4 * e4) : zero;
-      if (e4 < d4) *(f32x4*)(st_new + (size_t)a.Bm * a.d + 4 * e4) = r[i];
+      if (e4 < d4) *(f32x4*)(st_new + (size_t)a.Bm * slot + 4 * e4) = r[i];
       ss[0] += r[i][0] * r[i][0] + r[i][1] * r[i][1] + r[i][2] * r[i][2] + r[i][3] * r[i][3];
     }
     if (inf.next_ref_row < 0) return;
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
   const bool has_skip = a.valid_old[qb] != 0;
   const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;
-  const float* g_row = st_old + (size_t)b * a.d;
+  const float* g_row = st_old + (size_t)b * slot;
 
   f32x4 ev[IT], gv[IT];
   float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   const int nrow = a.next_row[qb];
   const float ms = (take ? acc[2] : acc[4]) / (float)a.d;
   const float scale = alive ? 1.0f / sqrtf(ms + a.eps) : 0.f;
-  float* out = st_new + (size_t)b * a.d;
+  float* out = st_new + (size_t)b * slot;
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
     const int e4 = threadIdx.x + i * SELR_THREADS;
@@ -285,32 +288,208 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   }
 }
 
+// Select for r-token states (window r = ItemSeq::win, 1..WIN_MAX): the cosine is taken over
+// the flattened r x d state (sums over all r rows), the decision is the one above, and each
+// kept token row gets its own RMSNorm scale for the next item's activations.  Two passes
+// over the rows (the second re-reads the kept rows).
+constexpr int SELW_THREADS = 512;
+constexpr int SELW_SUMS = 5 + 2 * WIN_MAX;  // rr, er, ee, gr, gg, ee_t[r], gg_t[r]
+
+template <class T>
+__global__ __launch_bounds__(SELW_THREADS) void select_win_kernel(SelectArgs a) {
+  const int q = blockIdx.x / (a.B + 1);
+  const int b = blockIdx.x % (a.B + 1);
+  const bool is_ref = b == a.B;
+  const ItemSeq inf = a.info[q];
+  const int r = inf.win;
+  const int d4 = a.d / 4;
+  const size_t slot = (size_t)a.wmax * a.d;
+  const size_t sstride = (size_t)(a.Bm + 1) * slot;
+  const float* st_old = a.state_old + q * sstride;
+  float* st_new = a.state_new + q * sstride;
+  const float* ref = a.E + (size_t)inf.ref_row * a.d;  // r consecutive rows
+  __shared__ float scratch[SELW_SUMS * (SELW_THREADS / 64)];
+
+  if (is_ref) {
+    float ss[WIN_MAX];
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) {
+      if (t >= r) continue;
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SELW_THREADS) {
+        const f32x4 x = *(const f32x4*)(ref + (size_t)t * a.d + 4 * e4);
+        *(f32x4*)(st_new + (size_t)a.Bm * slot + (size_t)t * a.d + 4 * e4) = x;
+        ss[t] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      }
+    }
+    if (inf.next_ref_row < 0) return;
+    block_sum<WIN_MAX, SELW_THREADS>(ss, scratch);
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) {
+      if (t >= r) continue;
+      const float scale = 1.0f / sqrtf(ss[t] / (float)a.d + a.eps);
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SELW_THREADS) {
+        const f32x4 x = *(const f32x4*)(st_new + (size_t)a.Bm * slot + (size_t)t * a.d + 4 * e4);
+        store_act<T>(a.xa_next, inf.next_ref_row + t, a.d, e4, x, scale);
+      }
+    }
+    return;
+  }
+
+  const int qb = q * a.Bm + b;
+  const int erow = a.exec_row[qb];
+  const int src = b - inf.w;
+  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
+  const bool has_skip = a.valid_old[qb] != 0;
+  const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;  // r consecutive rows
+  const float* g_row = st_old + (size_t)b * slot;                    // r rows of the slot
+
+  float acc[SELW_SUMS];
+#pragma unroll
+  for (int i = 0; i < SELW_SUMS; ++i) acc[i] = 0.f;
+  if (has_exec || has_skip) {
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) {
+      if (t >= r) continue;
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SELW_THREADS) {
+        const size_t o = (size_t)t * a.d + 4 * e4;
+        const f32x4 rv = *(const f32x4*)(ref + o);
+        acc[0] += rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2] + rv[3] * rv[3];
+        if (has_exec) {
+          const f32x4 ev = *(const f32x4*)(e_row + o);
+          acc[1] += ev[0] * rv[0] + ev[1] * rv[1] + ev[2] * rv[2] + ev[3] * rv[3];
+          const float ee = ev[0] * ev[0] + ev[1] * ev[1] + ev[2] * ev[2] + ev[3] * ev[3];
+          acc[2] += ee;
+          acc[5 + t] += ee;
+        }
+        if (has_skip) {
+          const f32x4 gv = *(const f32x4*)(g_row + o);
+          acc[3] += gv[0] * rv[0] + gv[1] * rv[1] + gv[2] * rv[2] + gv[3] * rv[3];
+          const float gg = gv[0] * gv[0] + gv[1] * gv[1] + gv[2] * gv[2] + gv[3] * gv[3];
+          acc[4] += gg;
+          acc[5 + WIN_MAX + t] += gg;
+        }
+      }
+    }
+  }
+  block_sum<SELW_SUMS, SELW_THREADS>(acc, scratch);
+  const float c_e = has_exec ? nan_to_ninf(acc[1] / (sqrtf(acc[2]) * sqrtf(acc[0]))) : -INFINITY;
+  const float c_s = has_skip ? nan_to_ninf(acc[3] / (sqrtf(acc[4]) * sqrtf(acc[0]))) : -INFINITY;
+  const bool take = c_e > c_s;
+  const float best = take ? c_e : c_s;
+  bool alive = best > -INFINITY;
+  if (best < a.tau) alive = false;
+  if (a.skip_cap >= 0 && inf.prefix - b > a.skip_cap) alive = false;
+
+  if (threadIdx.x == 0) {
+    a.valid_new[qb] = alive ? 1 : 0;
+    const size_t cell = ((size_t)q * a.n_items + a.item) * a.Bm + b;
+    if (a.decisions) a.decisions[cell] = alive ? (take ? 1 : 0) : 255;
+    if (a.margins) {
+      const bool he = c_e > -INFINITY, hs = c_s > -INFINITY;
+      a.margins[cell] = (he && hs) ? fabsf(c_e - c_s) : ((he != hs) ? INFINITY : NAN);
+    }
+    if (a.item == a.n_items - 1) a.cos_out[qb] = alive ? best : NAN;
+  }
+  if (threadIdx.x < a.mw) {
+    const int wd = threadIdx.x;
+    uint64_t mval = 0;
+    if (alive) {
+      if (take) {
+        mval = a.mask_old[((size_t)q * a.Bm + src) * a.mw + wd];
+        if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
+      } else {
+        mval = a.mask_old[(size_t)qb * a.mw + wd];
+      }
+    }
+    a.mask_new[(size_t)qb * a.mw + wd] = mval;
+  }
+
+  const int nrow = a.next_row[qb];
+  float* out = st_new + (size_t)b * slot;
+#pragma unroll
+  for (int t = 0; t < WIN_MAX; ++t) {
+    if (t >= r) continue;
+    const float ms = (take ? acc[5 + t] : acc[5 + WIN_MAX + t]) / (float)a.d;
+    const float scale = alive ? 1.0f / sqrtf(ms + a.eps) : 0.f;
+    const float* xr = (take ? e_row : g_row) + (size_t)t * a.d;
+    for (int e4 = threadIdx.x; e4 < d4; e4 += SELW_THREADS) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 x = alive ? *(const f32x4*)(xr + 4 * e4) : zero;
+      if (alive) *(f32x4*)(out + (size_t)t * a.d + 4 * e4) = x;
+      if (nrow >= 0) store_act<T>(a.xa_next, nrow + t, a.d, e4, x, scale);
+    }
+  }
+}
+
+// Greedy-token reduction over one vocabulary chunk: one wave per row.
+__global__ __launch_bounds__(256) void lm_argmax_kernel(LmArgmaxArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.R) return;
+  const int lane = threadIdx.x & 63;
+  const size_t sstride = (size_t)a.R * a.ldp;
+  const float* p = a.P + (size_t)row * a.ldp;
+  float bv = -INFINITY;
+  int bi = -1;
+  for (int c = lane; c < a.ncols; c += 64) {
+    float v = p[c];
+    for (int s = 1; s < a.splits; ++s) v += p[s * sstride + c];
+    if (v > bv) {  // ascending columns per lane: the first of equal values stays
+      bv = v;
+      bi = c;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    if (a.first) {
+      a.best_val[row] = bv;
+      a.best_idx[row] = bi < 0 ? -1 : a.col0 + bi;
+    } else if (bi >= 0 && (a.best_idx[row] < 0 || bv > a.best_val[row])) {
+      a.best_val[row] = bv;
+      a.best_idx[row] = a.col0 + bi;
+    }
+  }
+}
+
 // DP start: budget 0 and the reference hold x0; every other budget is empty.
 template <class T>
 __global__ __launch_bounds__(SEL_THREADS) void init_kernel(InitArgs a) {
   const int q = blockIdx.x;
-  const float* x0 = a.x0[q];
-  const size_t sstride = (size_t)(a.Bm + 1) * a.d;
+  const float* x0 = a.x0[q];  // [r][d]
+  const int r0 = a.rows[4 * q], rref = a.rows[4 * q + 1], win = a.rows[4 * q + 2];
+  const size_t slot = (size_t)a.wmax * a.d;
+  const size_t sstride = (size_t)(a.Bm + 1) * slot;
   float* st = a.state + q * sstride;
   for (int b = threadIdx.x; b < a.Bm; b += SEL_THREADS) a.valid[q * a.Bm + b] = b == 0 ? 1 : 0;
   for (int i = threadIdx.x; i < a.Bm * a.mw; i += SEL_THREADS)
     a.masks[(size_t)q * a.Bm * a.mw + i] = 0;
   __shared__ float scratch[SEL_THREADS / 64];
   const int d4 = a.d / 4;
-  float ss[1] = {0.f};
-  for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
-    const f32x4 x = *(const f32x4*)(x0 + 4 * e4);
-    *(f32x4*)(st + 4 * e4) = x;
-    *(f32x4*)(st + (size_t)a.Bm * a.d + 4 * e4) = x;
-    ss[0] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-  }
-  block_sum<1>(ss, scratch);
-  const float scale = 1.0f / sqrtf(ss[0] / (float)a.d + a.eps);
-  const int r0 = a.rows[2 * q], rref = a.rows[2 * q + 1];
-  for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
-    const f32x4 x = *(const f32x4*)(x0 + 4 * e4);
-    if (r0 >= 0) store_act<T>(a.xa, r0, a.d, e4, x, scale);
-    if (rref >= 0) store_act<T>(a.xa, rref, a.d, e4, x, scale);
+  for (int t = 0; t < win; ++t) {
+    const float* xt = x0 + (size_t)t * a.d;
+    float ss[1] = {0.f};
+    for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+      const f32x4 x = *(const f32x4*)(xt + 4 * e4);
+      *(f32x4*)(st + (size_t)t * a.d + 4 * e4) = x;
+      *(f32x4*)(st + (size_t)a.Bm * slot + (size_t)t * a.d + 4 * e4) = x;
+      ss[0] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
+    block_sum<1>(ss, scratch);
+    const float scale = 1.0f / sqrtf(ss[0] / (float)a.d + a.eps);
+    for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+      const f32x4 x = *(const f32x4*)(xt + 4 * e4);
+      if (r0 >= 0) store_act<T>(a.xa, r0 + t, a.d, e4, x, scale);
+      if (rref >= 0) store_act<T>(a.xa, rref + t, a.d, e4, x, scale);
+    }
   }
 }
 
@@ -337,10 +516,23 @@ static void launch_select_t(const SelectArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  if (a.act == ACT_F32)
+  if (a.rmax > 1) {  // some sequence holds r > 1 token states
+    const dim3 grid(a.n_seqs * (a.B + 1));
+    if (a.act == ACT_F32)
+      hipLaunchKernelGGL(select_win_kernel<float>, grid, dim3(SELW_THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL(select_win_kernel<bf16>, grid, dim3(SELW_THREADS), 0, s, a);
+  } else if (a.act == ACT_F32) {
     launch_select_t<float>(a, s);
-  else
+  } else {
     launch_select_t<bf16>(a, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_argmax(const LmArgmaxArgs& a, hipStream_t s) {
+  if (a.R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lm_argmax_kernel, dim3((a.R + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -26,15 +26,18 @@ KNAPSPEC_F32 = 0
 KNAPSPEC_BF16 = 1
 KNAPSPEC_RETURN_DECISIONS = 1
 KNAPSPEC_RETURN_MARGINS = 2
+KNAPSPEC_ALPHA_LM_HEAD = 4
+KNAPSPEC_WINDOW_MAX = 8
 KERNEL_CLASSES = ["init", "gemm_qkv", "qkv_rope", "attention", "combine", "gemm_o",
-                  "gemm_gate_up", "gemm_down", "select"]
+                  "gemm_gate_up", "gemm_down", "select", "lm_head"]
 
 
 class knapspec_model_desc(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ff", C.c_int32),
                 ("dtype", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
-                ("max_budgets", C.c_int32), ("max_seqs", C.c_int32), ("max_ctx", C.c_int32)]
+                ("max_budgets", C.c_int32), ("max_seqs", C.c_int32), ("max_ctx", C.c_int32),
+                ("max_window", C.c_int32)]
 
 
 class knapspec_layer_weights(C.Structure):
@@ -50,7 +53,7 @@ class knapspec_latency_model(C.Structure):
 class knapspec_seq(C.Structure):
     _fields_ = [("ctx_len", C.c_int32), ("ctx_capacity", C.c_int32),
                 ("k_cache", C.POINTER(C.c_void_p)), ("v_cache", C.POINTER(C.c_void_p)),
-                ("x0", C.c_void_p)]
+                ("x0", C.c_void_p), ("window", C.c_int32)]
 
 
 class knapspec_solve_args(C.Structure):
@@ -65,7 +68,8 @@ class knapspec_result(C.Structure):
                 ("valid", C.POINTER(C.c_uint8)), ("t_draft", C.POINTER(C.c_double)),
                 ("item_weight", C.POINTER(C.c_int32)), ("best_budget", C.POINTER(C.c_int32)),
                 ("best_gamma", C.POINTER(C.c_int32)), ("best_tpt", C.POINTER(C.c_double)),
-                ("decisions", C.POINTER(C.c_uint8)), ("margins", C.POINTER(C.c_float))]
+                ("decisions", C.POINTER(C.c_uint8)), ("margins", C.POINTER(C.c_float)),
+                ("alpha", C.POINTER(C.c_float)), ("tokens", C.POINTER(C.c_int32))]
 
 
 # symbol -> (restype, argtypes); every entry point of include/knapspec.h
@@ -96,6 +100,7 @@ SIGNATURES = {
     "knapspec_fit_latency": (C.c_int, [C.POINTER(C.c_int32), C.POINTER(C.c_double), C.c_int32,
                                        C.POINTER(C.c_double), C.POINTER(C.c_double),
                                        C.POINTER(C.c_double)]),
+    "knapspec_set_lm_head": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
 }
 
 if not os.path.exists(LIB_PATH):
@@ -120,6 +125,7 @@ knapspec_last_error = lib.knapspec_last_error
 knapspec_abi_version = lib.knapspec_abi_version
 knapspec_profile_items = lib.knapspec_profile_items
 knapspec_fit_latency = lib.knapspec_fit_latency
+knapspec_set_lm_head = lib.knapspec_set_lm_head
 
 
 class KnapSpecError(RuntimeError):
@@ -182,7 +188,7 @@ def fit_latency(n, t):
 class Result:
     """Host arrays of one solve (numpy views of what the library filled)."""
 
-    def __init__(self, n_seqs, n_budgets, n_items, mw, flags):
+    def __init__(self, n_seqs, n_budgets, n_items, mw, flags, windows=None):
         self.masks = np.zeros((n_seqs, n_budgets, mw), dtype=np.uint64)
         self.cos = np.zeros((n_seqs, n_budgets), dtype=np.float32)
         self.valid = np.zeros((n_seqs, n_budgets), dtype=np.uint8)
@@ -195,13 +201,26 @@ class Result:
                           if flags & KNAPSPEC_RETURN_DECISIONS else None)
         self.margins = (np.zeros((n_seqs, n_items, n_budgets), dtype=np.float32)
                         if flags & KNAPSPEC_RETURN_MARGINS else None)
+        self.alpha = np.zeros((n_seqs, n_budgets), dtype=np.float32)
+        self.windows = [1] * n_seqs if windows is None else [max(1, int(w)) for w in windows]
+        # per sequence (n_budgets + 1) x window token ids, flat in sequence order
+        self.tokens_flat = np.full(sum((n_budgets + 1) * w for w in self.windows), -1,
+                                   dtype=np.int32)
         self.struct = knapspec_result(
             _ptr(self.masks, C.c_uint64), _ptr(self.cos, C.c_float), _ptr(self.valid, C.c_uint8),
             _ptr(self.t_draft, C.c_double), _ptr(self.item_weight, C.c_int32),
             _ptr(self.best_budget, C.c_int32), _ptr(self.best_gamma, C.c_int32),
             _ptr(self.best_tpt, C.c_double),
             _ptr(self.decisions, C.c_uint8) if self.decisions is not None else None,
-            _ptr(self.margins, C.c_float) if self.margins is not None else None)
+            _ptr(self.margins, C.c_float) if self.margins is not None else None,
+            _ptr(self.alpha, C.c_float), _ptr(self.tokens_flat, C.c_int32))
+
+    def tokens(self, q: int) -> np.ndarray:
+        """[n_budgets + 1][window] greedy tokens of sequence q (row n_budgets: full model)."""
+        B = self.alpha.shape[1]
+        off = sum((B + 1) * w for w in self.windows[:q])
+        w = self.windows[q]
+        return self.tokens_flat[off:off + (B + 1) * w].reshape(B + 1, w)
 
 
 class Model:
@@ -239,22 +258,25 @@ class Model:
             keep += [kp, vp]
             cap = int(sq["k_cache"][0].shape[1]) if self.n_layers else 0
             carr[i] = knapspec_seq(int(sq["ctx"]), cap, C.cast(kp, C.POINTER(C.c_void_p)),
-                                   C.cast(vp, C.POINTER(C.c_void_p)), sq["x0"].data_ptr())
+                                   C.cast(vp, C.POINTER(C.c_void_p)), sq["x0"].data_ptr(),
+                                   int(sq.get("window", 1)))
         return carr, keep
 
     def solve(self, seqs: List[dict], n_budgets: int, gamma, tau: float = -math.inf,
               max_skip_weight: int = -1, flags: int = 0, stream=None,
               result: Optional[Result] = None) -> Result:
         """seqs: dicts with ctx (int), k_cache / v_cache (lists of device tensors per layer,
-        [hkv][capacity][dh]), x0 (device float32 [d])."""
+        [hkv][capacity][dh]), x0 (device float32 [window][d] or [d]) and optionally window
+        (int, default 1)."""
         torch = self._torch
         S = len(seqs)
         carr, keep = self._seq_array(seqs)
         s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
         args = knapspec_solve_args(S, carr, int(n_budgets), int(gamma[0]), int(gamma[1]),
                                    float(tau), int(max_skip_weight), int(flags), C.c_void_p(s))
-        res = result if result is not None else Result(S, n_budgets, 2 * self.n_layers, self.mw,
-                                                        flags)
+        res = result if result is not None else Result(
+            S, n_budgets, 2 * self.n_layers, self.mw, flags,
+            windows=[int(sq.get("window", 1)) for sq in seqs])
         _check(knapspec_solve(self.handle, C.byref(args), C.byref(res.struct)), "knapspec_solve")
         return res
 
@@ -271,6 +293,13 @@ class Model:
                                       C.c_void_p(s), _ptr(attn, C.c_double), C.byref(mlp)),
                "knapspec_profile_items")
         return attn, mlp.value
+
+    def set_lm_head(self, w, vocab: int):
+        """knapspec_set_lm_head: w is a device tensor [vocab][d] in the model dtype (kept alive
+        here)."""
+        self._lm_head = w
+        _check(knapspec_set_lm_head(self.handle, C.c_void_p(w.data_ptr()), int(vocab)),
+               "knapspec_set_lm_head")
 
     def set_profiling(self, enable: bool):
         _check(knapspec_set_profiling(self.handle, 1 if enable else 0), "knapspec_set_profiling")

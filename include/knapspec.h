@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KNAPSPEC_ABI_VERSION 2
+#define KNAPSPEC_ABI_VERSION 3
 
 #define KNAPSPEC_OK 0
 #define KNAPSPEC_EINVAL (-1)       /* bad argument, shape or pointer */
@@ -53,6 +53,9 @@ extern "C" {
 
 #define KNAPSPEC_RETURN_DECISIONS 1 /* fill knapspec_result.decisions */
 #define KNAPSPEC_RETURN_MARGINS 2   /* fill knapspec_result.margins */
+#define KNAPSPEC_ALPHA_LM_HEAD 4    /* TPT acceptance from the LM head (knapspec_set_lm_head) */
+
+#define KNAPSPEC_WINDOW_MAX 8 /* largest r of an r-token window */
 
 typedef struct knapspec_model knapspec_model; /* opaque */
 
@@ -70,6 +73,8 @@ typedef struct {
   int32_t max_budgets; /* largest n_budgets a solve may use (2..1024) */
   int32_t max_seqs;    /* largest n_seqs a solve may use */
   int32_t max_ctx;     /* largest ctx_len a solve may use */
+  int32_t max_window;  /* largest r a sequence may use (0 or 1: single-token states;
+                          <= KNAPSPEC_WINDOW_MAX); the workspace scales with it */
 } knapspec_model_desc;
 
 /* Device pointers of one layer's weights, row-major [out][in], in desc.dtype:
@@ -102,14 +107,21 @@ int knapspec_set_latency_model(knapspec_model* model, const knapspec_latency_mod
 
 /* One sequence to solve for.  All pointers are device pointers borrowed for the call.
  *   k_cache[l], v_cache[l]: layer l's cache, [hkv][ctx_capacity][dh] in desc.dtype, holding
- *     positions 0 .. ctx_len-1 already rotated; the new token sits at position ctx_len.
- *   x0: float32 [d], the new token's input hidden state. */
+ *     positions 0 .. ctx_len-1 already rotated.
+ *   x0: float32 [window][d], the input hidden states of the window's tokens, token t at
+ *     position ctx_len + t.
+ *   window: r, the tokens per DP state (0 counts as 1; <= desc.max_window).  The review
+ *     gives the DP table as (2L+1) x (K+1) x r x d (referee major comment 4) over a window
+ *     of recent tokens (free parameter m).  Reading: the r tokens pass through each item as
+ *     one causal block (each attends to the cache and to window tokens 0..t), and states
+ *     are compared by the cosine of the flattened r x d matrices. */
 typedef struct {
   int32_t ctx_len;      /* 0 .. max_ctx */
   int32_t ctx_capacity; /* positions per KV head in the buffers, >= ctx_len */
   const void* const* k_cache; /* host array of n_layers device pointers */
   const void* const* v_cache; /* host array of n_layers device pointers */
   const float* x0;
+  int32_t window;
 } knapspec_seq;
 
 typedef struct {
@@ -137,6 +149,12 @@ typedef struct {
   uint8_t* decisions;   /* nullable [n_seqs][L2][n_budgets]: 0 skip, 1 execute, 255 invalid */
   float* margins;       /* nullable [n_seqs][L2][n_budgets]: |c_exec - c_skip|, +inf when one
                            option exists, NaN when none */
+  float* alpha;         /* nullable [n_seqs][n_budgets]: the acceptance estimate the TPT grid
+                           used (clamp(cos, 0, 1), or the LM-head estimate); 0 if invalid */
+  int32_t* tokens;      /* nullable: per sequence in order, (n_budgets + 1) x window_q
+                           entries: with KNAPSPEC_ALPHA_LM_HEAD, the greedy token of each
+                           window token of each budget's final state (budget n_budgets: the
+                           full model); -1 for invalid budgets and without the flag */
 } knapspec_result;
 
 /* Runs the whole DP for every sequence on the GPU: per item, one batched GEMM over all live
@@ -145,9 +163,19 @@ typedef struct {
  * cosine/select.  Enqueues on args->hip_stream, synchronises once, copies the per-budget
  * results to `result` and runs the TPT grid on the host with a = clamp(cos, 0, 1).
  * The acceptance proxy a = clamp(cos) stands in for the paper's history estimate (Eq. 9),
- * which the pages do not print. */
+ * which the pages do not print.  With KNAPSPEC_ALPHA_LM_HEAD (needs knapspec_set_lm_head)
+ * the grid instead uses, per budget, the fraction of the window's tokens whose greedy token
+ * -- argmax over the LM head of the RMSNorm'd final state, float32 logits, ties to the lower
+ * index -- equals the full model's (review, free parameters: the window is used "for DP and
+ * acceptance estimation"; reading of Eq. 9). */
 int knapspec_solve(knapspec_model* model, const knapspec_solve_args* args,
                    knapspec_result* result);
+
+/* LM head for the acceptance estimate: w [vocab][d_model] in desc.dtype, a borrowed device
+ * pointer kept alive and unchanged until the model is freed or the head replaced.  The
+ * first call allocates the device buffers the estimate needs (a running argmax per row);
+ * EINVAL for a NULL pointer or vocab outside [1, 2^24], ENOMEM when allocation fails. */
+int knapspec_set_lm_head(knapspec_model* model, const void* w, int32_t vocab);
 
 /* Host-only TPT grid for caller-supplied acceptance estimates alpha[b] (any a in [0,1]).
  * Ties keep the smaller budget, then the smaller gamma.  Writes -1/-1/NaN when no budget is
@@ -190,7 +218,7 @@ int knapspec_fit_latency(const int32_t* n, const double* t, int32_t count, doubl
  * time to one of the kernel classes below.  Enabling (enable = 1) resets the counters;
  * knapspec_get_kernel_times copies them (n_classes entries, at most KNAPSPEC_KERNEL_CLASSES).
  * Profiling adds two event records per launch and does not change any result. */
-#define KNAPSPEC_KERNEL_CLASSES 9
+#define KNAPSPEC_KERNEL_CLASSES 10
 #define KNAPSPEC_K_INIT 0
 #define KNAPSPEC_K_GEMM_QKV 1
 #define KNAPSPEC_K_QKV_ROPE 2
@@ -200,6 +228,7 @@ int knapspec_fit_latency(const int32_t* n, const double* t, int32_t count, doubl
 #define KNAPSPEC_K_GEMM_GATE_UP 6
 #define KNAPSPEC_K_GEMM_DOWN 7
 #define KNAPSPEC_K_SELECT 8 /* split/residual reduce + cosine select + next-item RMSNorm */
+#define KNAPSPEC_K_LM_HEAD 9 /* LM-head GEMM + greedy-token reduction (acceptance estimate) */
 int knapspec_set_profiling(knapspec_model* model, int32_t enable);
 int knapspec_get_kernel_times(const knapspec_model* model, double* total_ms, int64_t* launches,
                               int32_t n_classes);

@@ -104,3 +104,68 @@ def compare(oracle: ko.SolveResult, gpu_res, seq: int, beta: float, apply_item, 
     return ParityReport(cells=cells, clean=int(clean.sum()), excused=int((~clean).sum()),
                         mismatched_clean=mism, p2_max_err=p2, p3_bad=p3_bad, p4_ok=bool(p4),
                         same_pick=bool(same_pick), max_cos_diff_same_mask=dcos)
+
+
+def forward_states(apply_item, n_items: int, x0, bits: np.ndarray):
+    """The oracle's final states for each subset row of ``bits`` [R][n_items] and the full
+    model's (every item), from the same input x0 ([d] or [r][d])."""
+    R = bits.shape[0]
+    x0 = np.asarray(x0, dtype=np.float32)
+    rows = np.repeat(x0[None], R + 1, axis=0)
+    for i in range(n_items):
+        sel = np.concatenate([np.nonzero(bits[:, i])[0], [R]])
+        rows[sel] = apply_item(i, rows[sel])
+    return rows[:R], rows[R]
+
+
+@dataclasses.dataclass
+class AlphaReport:
+    budgets: int
+    tokens: int
+    excused_tokens: int
+    mismatched_tokens: int
+    alpha_mismatch: int
+
+    def line(self) -> str:
+        return (f"budgets={self.budgets} tokens={self.tokens} excused={self.excused_tokens} "
+                f"token_mismatch={self.mismatched_tokens} alpha_mismatch={self.alpha_mismatch}")
+
+
+def compare_alpha(gpu_res, seq: int, apply_item, x0, w_lm, eps: float, band: float,
+                  n_items: int) -> AlphaReport:
+    """P5: every valid GPU budget's greedy tokens (and the full model's) against the oracle's
+    greedy tokens of the oracle's forward of the GPU's own mask; a window token whose oracle
+    top-2 logit margin (for the budget or for the full model) is below ``band`` is excused.
+    The GPU's alpha must equal the match fraction of its own tokens, and equal the oracle's
+    wherever no token of the budget is excused."""
+    valid = gpu_res.valid[seq].astype(bool)
+    vb = np.nonzero(valid)[0]
+    tok_g = gpu_res.tokens(seq)                   # [B+1][r]
+    r = tok_g.shape[1]
+    B = valid.shape[0]
+    bits = ko.unpack_masks(gpu_res.masks[seq], n_items)[vb]
+    st, ref = forward_states(apply_item, n_items, x0, bits)
+    st = st.reshape(len(vb), r, -1)
+    ref = np.asarray(ref).reshape(r, -1)
+    tok_o, mar_o = ko.greedy_tokens(st, w_lm, eps)
+    tref_o, mref_o = ko.greedy_tokens(ref, w_lm, eps)
+    clean_ref = mref_o >= band
+    # the full model's tokens
+    mism = int(np.sum((tok_g[B] != tref_o) & clean_ref))
+    excused = int(np.sum(~clean_ref))
+    alpha_bad = 0
+    for k, b in enumerate(vb):
+        clean = (mar_o[k] >= band) & clean_ref
+        excused += int(np.sum(~clean))
+        mism += int(np.sum((tok_g[b] != tok_o[k]) & clean))
+        # alphas are match counts over r, returned in float32
+        a_self = float(np.sum(tok_g[b] == tok_g[B])) / r
+        if abs(float(gpu_res.alpha[seq][b]) - a_self) > 1e-6:
+            alpha_bad += 1
+        if clean.all():
+            a_orc = float(np.sum(tok_o[k] == tref_o)) / r
+            alpha_bad += int(abs(float(gpu_res.alpha[seq][b]) - a_orc) > 1e-6)
+    assert np.all(gpu_res.alpha[seq][~valid] == 0.0)
+    assert np.all(tok_g[np.nonzero(~valid)[0]] == -1)
+    return AlphaReport(budgets=len(vb), tokens=(len(vb) + 1) * r, excused_tokens=excused,
+                       mismatched_tokens=mism, alpha_mismatch=alpha_bad)

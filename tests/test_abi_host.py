@@ -35,7 +35,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(ks):
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     out = subprocess.run(["nm", "-D", "--defined-only", ks.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (knapspec_\w+)", out))
@@ -48,7 +48,7 @@ def test_exports_every_declared_symbol(ks):
 
 
 def test_version_and_mask_words(ks):
-    assert ks.knapspec_abi_version() == 2
+    assert ks.knapspec_abi_version() == 3
     assert [ks.knapspec_mask_words(n) for n in (1, 8, 32, 33, 80)] == [1, 1, 1, 2, 3]
 
 
@@ -141,7 +141,7 @@ def _load(ks, desc, null_weight=False):
 def test_load_model_validation(ks):
     bad = [dict(n_q_heads=3), dict(head_dim=63), dict(dtype=7), dict(max_budgets=1),
            dict(max_budgets=5000), dict(max_seqs=0), dict(max_ctx=-1), dict(rms_eps=0.0),
-           dict(d_model=0)]
+           dict(d_model=0), dict(max_window=-1), dict(max_window=ks.KNAPSPEC_WINDOW_MAX + 1)]
     for kw in bad:
         rc, _ = _load(ks, _desc(ks, **kw))
         assert rc == ks.KNAPSPEC_EINVAL, kw
@@ -211,3 +211,18 @@ def test_profile_items_rejects_null_model(ks):
     n = (C.c_int32 * 1)(0)
     rc = ks.knapspec_profile_items(None, None, n, 1, 1, None, out, C.byref(mlp))
     assert rc == ks.KNAPSPEC_EINVAL
+
+
+def test_set_lm_head_rejects_null_model(ks):
+    assert ks.knapspec_set_lm_head(None, 0x1000, 64) == ks.KNAPSPEC_EINVAL
+    assert b"NULL" in ks.knapspec_last_error()
+
+
+def test_window_struct_layout(ks):
+    import ctypes as C
+
+    # the appended fields sit at the end of their C structs (ABI version 3)
+    assert ks.knapspec_model_desc.max_window.offset == 12 * 4
+    # ctx_len, ctx_capacity (int32), k_cache, v_cache, x0 (pointers), then window
+    assert ks.knapspec_seq.window.offset == 8 + 3 * C.sizeof(C.c_void_p)
+    assert ks.knapspec_result.tokens.offset == ks.knapspec_result.alpha.offset + C.sizeof(C.c_void_p)

@@ -27,7 +27,7 @@ class DeviceProblem:
 
     def __init__(self, wl: Workload, seed: int = 0, ctxs: Optional[List[int]] = None,
                  caps: Optional[List[int]] = None, keep_host: bool = False,
-                 max_budgets: Optional[int] = None):
+                 max_budgets: Optional[int] = None, window: int = 1, lm_vocab: int = 0):
         import torch
 
         from draft_layer_selection_amd import knapspec as ks
@@ -55,7 +55,11 @@ class DeviceProblem:
                 self.v_cache[q].append(_to_device(v, s.dtype, torch))
                 if keep_host:
                     self.host_kv[q].append((k, v))
-        self.host_x0 = [synth.x0(wl, q, 0, seed) for q in range(len(self.ctxs))]
+        # r-token window: x0 [r][d] per sequence (r = 1 keeps the single-token [d] layout)
+        self.window = max(1, int(window))
+        self.host_x0 = [synth.x0(wl, q, 0, seed) if self.window == 1
+                        else synth.x0_window(wl, self.window, q, 0, seed)
+                        for q in range(len(self.ctxs))]
         self.x0 = [torch.from_numpy(x).to("cuda") for x in self.host_x0]
         # inputs of the re-solve schedule (multi-sequence presets): x0 of every (seq, resolve),
         # resident on the device up front
@@ -69,11 +73,20 @@ class DeviceProblem:
                     dtype=ks.KNAPSPEC_BF16 if s.dtype == "bf16" else ks.KNAPSPEC_F32,
                     rms_eps=s.rms_eps, rope_theta=s.rope_theta,
                     max_budgets=max_budgets or wl.n_budgets, max_seqs=len(self.ctxs),
-                    max_ctx=max(self.caps))
+                    max_ctx=max(self.caps), max_window=self.window)
         torch.cuda.synchronize()
         self.model = ks.Model(desc, self.layers)
         lat = wl.latency
         self.model.set_latency(lat.attn_base, lat.attn_per_token, lat.mlp, lat.fixed)
+        # LM head of the acceptance estimate: host copy (widened) for the oracle, device copy
+        # in the model dtype for the library
+        self.lm_vocab = int(lm_vocab)
+        self.host_lm = None
+        if self.lm_vocab:
+            self.host_lm = synth.lm_head(wl, self.lm_vocab, seed)
+            raw = synth.lm_head(wl, self.lm_vocab, seed, bits=True)
+            self.lm = _to_device(raw, s.dtype, torch)
+            self.model.set_lm_head(self.lm, self.lm_vocab)
 
     def set_x0(self, q: int, x: np.ndarray):
         self.host_x0[q] = x
@@ -88,7 +101,7 @@ class DeviceProblem:
         x0 = ([self.resolve_x0_dev[q][resolve] for q in range(len(ctxs))] if resolve is not None
               else self.x0)
         return [{"ctx": ctxs[q], "k_cache": self.k_cache[q], "v_cache": self.v_cache[q],
-                 "x0": x0[q]} for q in range(len(ctxs))]
+                 "x0": x0[q], "window": self.window} for q in range(len(ctxs))]
 
     def resolve_ctxs(self, r: int) -> List[int]:
         return [c + r * self.wl.tokens_per_resolve for c in self.ctxs]
