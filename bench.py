@@ -43,24 +43,26 @@ def item_rows(w, B):
     return rows, live
 
 
-def algorithmic_work(wl, w_per_seq, ctxs):
+def algorithmic_work(wl, w_per_seq, ctxs, window=1, vocab=0):
     """Minimum HBM bytes and FLOPs of one solve, per kernel class and in total.
 
     Per item: its weight matrix once; for Attention items the sequence's K and V cache once;
     the activation rows it reads and the rows it writes once; and for the state a read of every
-    source row plus a write of every live budget (fp32)."""
+    source row plus a write of every live budget (fp32).  With an r-token window every
+    budget row is r token rows; with an LM head of ``vocab`` rows the acceptance estimate
+    reads the head once and the (budgets + 1) x r final rows."""
     s = wl.shape
     eb = s.elem_bytes
     d, ff, dh, hq, hkv = s.d_model, s.d_ff, s.head_dim, s.n_q_heads, s.n_kv_heads
     qd, nqkv = hq * dh, (hq + 2 * hkv) * dh
     cls = {k: {"bytes": 0.0, "flops": 0.0, "launches": 0} for k in
            ("gemm_qkv", "qkv_rope", "attention", "combine", "gemm_o", "gemm_gate_up",
-            "gemm_down", "select")}
+            "gemm_down", "select", "lm_head")}
     L2 = 2 * s.n_layers
     per_item_rows = []
     for q, w in enumerate(w_per_seq):
         rows, live = item_rows(list(w), wl.n_budgets)
-        per_item_rows.append((rows, live))
+        per_item_rows.append(([x * window for x in rows], [x * window for x in live]))
     for i in range(L2):
         R = sum(pr[0][i] for pr in per_item_rows)
         V = sum(pr[1][i] for pr in per_item_rows)
@@ -97,9 +99,15 @@ def algorithmic_work(wl, w_per_seq, ctxs):
         c = cls["select"]
         c["bytes"] += (R + V) * d * 4
         c["launches"] += 1
-    w_bytes = s.n_layers * (s.attn_weight_bytes() + s.mlp_weight_bytes())
+    if vocab:
+        c = cls["lm_head"]
+        Rlm = len(w_per_seq) * (wl.n_budgets + 1) * window
+        c["bytes"] += vocab * d * eb + Rlm * d * eb
+        c["flops"] += 2.0 * Rlm * vocab * d
+        c["launches"] += 1
+    w_bytes = s.n_layers * (s.attn_weight_bytes() + s.mlp_weight_bytes()) + vocab * d * eb
     kv_bytes = sum(2 * hkv * c_ * dh * eb * s.n_layers for c_ in ctxs)
-    state_bytes = cls["select"]["bytes"]
+    state_bytes = cls["select"]["bytes"] + (cls["lm_head"]["bytes"] - vocab * d * eb)
     total_bytes = w_bytes + kv_bytes + state_bytes
     total_flops = sum(cls[k]["flops"] for k in cls)
     return cls, {"weight_bytes": w_bytes, "kv_bytes": kv_bytes, "state_bytes": state_bytes,
@@ -272,6 +280,10 @@ def main():
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--commands", default="")
+    ap.add_argument("--window", type=int, default=1,
+                    help="tokens per DP state (r-token window); 1 = the single-token solve")
+    ap.add_argument("--lm-vocab", type=int, default=0,
+                    help="also run the LM-head acceptance estimate with this many rows")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args)
@@ -295,7 +307,11 @@ def main():
     want_cpu = not args.no_cpu_baseline
     t0 = time.time()
     log(f"[bench] generating and uploading {wl.name} inputs ...")
-    prob = DeviceProblem(wl, args.seed, keep_host=want_cpu)
+    if args.window != 1 or args.lm_vocab:
+        want_cpu = False  # the CPU baseline leg covers the single-token solve only
+    prob = DeviceProblem(wl, args.seed, keep_host=want_cpu, window=args.window,
+                         lm_vocab=args.lm_vocab)
+    flags = prob.ks.KNAPSPEC_ALPHA_LM_HEAD if args.lm_vocab else 0
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; warmup {args.warmup}")
     # one step = one solve; for a multi-sequence preset one step is its whole re-solve
     # schedule (every sequence re-solved `resolves` times as its context grows)
@@ -304,9 +320,9 @@ def main():
 
     def step(res):
         if not multi:
-            return prob.solve(result=res)
+            return prob.solve(result=res, flags=flags)
         for r in range(prob.n_resolves):
-            res = prob.solve(resolve=r)
+            res = prob.solve(resolve=r, flags=flags)
         return res
 
     res = None
@@ -343,7 +359,7 @@ def main():
     for r in range(prob.n_resolves):
         ctxs = prob.resolve_ctxs(r) if multi else prob.ctxs
         w_per_seq = [ko_weights(wl, c) for c in ctxs]
-        c_r, t_r = algorithmic_work(wl, w_per_seq, ctxs)
+        c_r, t_r = algorithmic_work(wl, w_per_seq, ctxs, args.window, args.lm_vocab)
         if cls is None:
             cls, tot = c_r, t_r
         else:
@@ -413,6 +429,7 @@ def main():
                    "heads_q_kv": [wl.shape.n_q_heads, wl.shape.n_kv_heads],
                    "head_dim": wl.shape.head_dim, "d_ff": wl.shape.d_ff, "ctx": prob.ctxs,
                    "budgets": wl.n_budgets, "gamma": list(wl.gamma), "n_seqs": len(prob.ctxs),
+                   "window": args.window, "lm_vocab": args.lm_vocab,
                    "parallelism": "single-gpu"},
         "achieved_hbm_gbs": round(achieved_gbs, 1),
         "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),

@@ -460,7 +460,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------
 // combine: one wave per (row, query head).  All maxima are in the log2 domain.
 // ------------------------------------------------------------------------------------
-template <class T, int DH>
+template <class T, int DH, int WK>  // WK: largest window token count of the launch (1 or 8)
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int EPL = DH / 64;  // consecutive dh elements per lane
   const int widx = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -474,10 +474,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const T* q = (const T*)a.Q + ((size_t)r * a.hq + h) * DH + e0;
   // window keys: the own keys of the rows of window tokens 0..tw of this state (tw = 0: the
   // row's own key only)
-  const int tw = a.row_tok[r];
-  float s_w[WIN_MAX];
+  const int tw = WK == 1 ? 0 : a.row_tok[r];
+  float s_w[WK];
 #pragma unroll
-  for (int k = 0; k < WIN_MAX; ++k) {
+  for (int k = 0; k < WK; ++k) {
     s_w[k] = -INFINITY;
     if (k <= tw) {
       const float* ks = a.kself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
@@ -498,15 +498,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const float ls = has ? a.Lpart[slot0 + lane * split_stride] : 0.f;
   float mx = fmaxf(warp_max(ms), s_w[0]);
 #pragma unroll
-  for (int k = 1; k < WIN_MAX; ++k)
+  for (int k = 1; k < WK; ++k)
     if (k <= tw) mx = fmaxf(mx, s_w[k]);
   const float wsp = has ? exp2f(ms - mx) : 0.f;
-  float w_w[WIN_MAX];
+  float w_w[WK];
 #pragma unroll
-  for (int k = 0; k < WIN_MAX; ++k) w_w[k] = k <= tw ? exp2f(s_w[k] - mx) : 0.f;
+  for (int k = 0; k < WK; ++k) w_w[k] = k <= tw ? exp2f(s_w[k] - mx) : 0.f;
   float den = warp_sum(wsp * ls) + w_w[0];
 #pragma unroll
-  for (int k = 1; k < WIN_MAX; ++k)
+  for (int k = 1; k < WK; ++k)
     if (k <= tw) den += w_w[k];
   const float inv = 1.0f / den;
   float num[EPL];
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int e = 0; e < EPL; ++e) num[e] = w_w[0] * vs[e];
   }
 #pragma unroll
-  for (int k = 1; k < WIN_MAX; ++k) {
+  for (int k = 1; k < WK; ++k) {
     if (k <= tw) {
       const float* vs = a.vself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
 #pragma unroll
@@ -579,20 +579,28 @@ hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t 
   return hipGetLastError();
 }
 
+template <class T, int DH>
+static void launch_combine_t(const CombineArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.rmax > 1)
+    hipLaunchKernelGGL((combine_kernel<T, DH, WIN_MAX>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, DH, 1>), grid, block, 0, s, a);
+}
+
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s) {
   const int waves = a.R * a.hq;
   const dim3 grid((waves + 3) / 4), block(256);
   if (a.dh != 64 && a.dh != 128) return hipErrorInvalidValue;
   if (act == ACT_F32) {
     if (a.dh == 64)
-      hipLaunchKernelGGL((combine_kernel<float, 64>), grid, block, 0, s, a);
+      launch_combine_t<float, 64>(a, grid, block, s);
     else
-      hipLaunchKernelGGL((combine_kernel<float, 128>), grid, block, 0, s, a);
+      launch_combine_t<float, 128>(a, grid, block, s);
   } else {
     if (a.dh == 64)
-      hipLaunchKernelGGL((combine_kernel<bf16, 64>), grid, block, 0, s, a);
+      launch_combine_t<bf16, 64>(a, grid, block, s);
     else
-      hipLaunchKernelGGL((combine_kernel<bf16, 128>), grid, block, 0, s, a);
+      launch_combine_t<bf16, 128>(a, grid, block, s);
   }
   return hipGetLastError();
 }

@@ -87,6 +87,7 @@ struct CombineArgs {
   const float* vself;
   const int* row_tok;  // [R] window token t of the row: it also attends to the own
                        // keys/values of rows r - t .. r (window tokens 0..t of its state)
+  int rmax;            // largest window r of the launch's rows (1: row_tok is not read)
   const float* Opart;
   const float* Mpart;
   const float* Lpart;

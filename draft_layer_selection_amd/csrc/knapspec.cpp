@@ -988,6 +988,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       ca.kself = m->kself;
       ca.vself = m->vself;
       ca.row_tok = d_rowtok + (size_t)i * m->Rmax;
+      ca.rmax = rmax;
       ca.Opart = m->Opart;
       ca.Mpart = m->Mpart;
       ca.Lpart = m->Lpart;
@@ -1493,6 +1494,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
         ca.seqs = (const ks::AttnSeq*)(dp + o_aseq);
         ca.row_seq = (const int*)(dp + o_rowseq);
         ca.row_tok = (const int*)(dp + o_rowtok);
+        ca.rmax = 1;
         ca.R = 1;
         ca.hq = hq;
         ca.hkv = hkv;
