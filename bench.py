@@ -270,7 +270,7 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=6)
+    ap.add_argument("--cpu-layers", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--summarize-profiles", action="store_true")
     ap.add_argument("--stats")
