@@ -32,6 +32,9 @@ Pins (tests that tie this code to something other than itself):
                                 loop-based attention on tiny inputs.
   * alpha_lm_head               the full-model state scores 1; planted LM heads with known
                                 greedy tokens; values on the grid {0, 1/r, ..., 1}.
+  * knapsack_dp_beam            beam 1 is knapsack_dp exactly; a beam at least as wide as the
+                                number of subsets of any weight is exhaustive enumeration
+                                (the best subset per budget, brute force on small decoders).
 Parity unpinned: the full DP at the Qwen3-1.7B, Llama-3-8B and Llama-3-70B shapes has no
 independent check beyond the pins above and the per-mask self-consistency of the results.
 """
@@ -383,6 +386,94 @@ def knapsack_dp(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: in
                     states=g, ref=ref)
 
 
+@dataclasses.dataclass
+class BeamResult:
+    bits: np.ndarray        # bool [B][k][n_items]; slot 0 is the budget's best set
+    valid: np.ndarray       # bool [B][k]
+    cos: np.ndarray         # float64 [B][k], NaN where invalid
+    states: np.ndarray      # float32 [B][k][...] final states
+    ref: np.ndarray
+
+    def best(self) -> DPResult:
+        """Slot 0 of every budget in DPResult form (no per-cell decisions or margins)."""
+        B, n_items = self.bits.shape[0], self.bits.shape[2]
+        return DPResult(bits=self.bits[:, 0].copy(), valid=self.valid[:, 0].copy(),
+                        cos=self.cos[:, 0].copy(),
+                        decisions=np.full((n_items, B), 255, dtype=np.uint8),
+                        margins=np.full((n_items, B), np.nan), states=self.states[:, 0].copy(),
+                        ref=self.ref)
+
+
+def knapsack_dp_beam(apply_item: Callable[[int, np.ndarray], np.ndarray], n_items: int,
+                     w: Sequence[int], x0: np.ndarray, n_budgets: int, beam: int,
+                     tau: float = -np.inf, skip_cap: int = -1) -> BeamResult:
+    """The DP with the top-``beam`` states kept per (item, budget) cell instead of one.
+
+    Review, "Reading between the lines": an exact-knapsack or beam-search variant of the
+    greedy rule shows how much headroom the one-state DP leaves.  Reading taken here: at item
+    i the candidates of budget b are the skip candidates (every state kept at b) and the
+    execute candidates (item i applied to every state kept at b - w_i); they are ranked by
+    cosine to the reference after item i, higher first, with exact ties ordering skip
+    candidates before execute candidates and then by the slot they came from; NaN ranks as
+    minus infinity and such candidates are dropped; the first ``beam`` survive.  tau and the
+    skip cap act as in knapsack_dp.  beam = 1 is knapsack_dp; a beam at least the number of
+    subsets of any one weight keeps every subset, i.e. enumeration.
+    """
+    B, k = int(n_budgets), int(beam)
+    assert k >= 1
+    x0 = np.asarray(x0, dtype=F32)
+    g = np.zeros((B, k) + x0.shape, dtype=F32)
+    valid = np.zeros((B, k), dtype=bool)
+    bits = np.zeros((B, k, n_items), dtype=bool)
+    cosv = np.full((B, k), np.nan)
+    g[0, 0] = x0
+    valid[0, 0] = True
+    ref = x0.copy()
+    prefix = 0
+    for i in range(n_items):
+        wi = int(w[i])
+        prefix += wi
+        src = [(b, j) for b in range(max(0, B - wi)) for j in range(k) if valid[b, j]]
+        rows = np.concatenate([np.stack([g[b, j] for b, j in src])
+                               if src else np.zeros((0,) + x0.shape, F32), ref[None]], axis=0)
+        out = apply_item(i, rows)
+        ref_new = out[-1].astype(F32)
+        ex = {src[m]: out[m] for m in range(len(src))}
+        new_g = np.zeros_like(g)
+        new_valid = np.zeros_like(valid)
+        new_bits = np.zeros_like(bits)
+        new_cos = np.full((B, k), np.nan)
+        for b in range(B):
+            cands = []  # (cos, kind 0 skip / 1 exec, slot, state, bits)
+            for j in range(k):
+                if valid[b, j]:
+                    cands.append((g[b, j], 0, j, bits[b, j]))
+            if b - wi >= 0:
+                for j in range(k):
+                    if (b - wi, j) in ex:
+                        nb = bits[b - wi, j].copy()
+                        nb[i] = True
+                        cands.append((ex[(b - wi, j)], 1, j, nb))
+            if not cands:
+                continue
+            c = cos_rows(np.stack([cd[0] for cd in cands]), ref_new)
+            c = np.where(np.isnan(c), -np.inf, c)
+            order = sorted(range(len(cands)), key=lambda m: (-c[m], cands[m][1], cands[m][2]))
+            if skip_cap >= 0 and prefix - b > skip_cap:
+                continue
+            kept = 0
+            for m in order:
+                if kept == k or not (c[m] > -np.inf) or c[m] < tau:
+                    break
+                new_g[b, kept] = cands[m][0]
+                new_bits[b, kept] = cands[m][3]
+                new_valid[b, kept] = True
+                new_cos[b, kept] = c[m]
+                kept += 1
+        g, valid, bits, cosv, ref = new_g, new_valid, new_bits, new_cos, ref_new
+    return BeamResult(bits=bits, valid=valid, cos=cosv, states=g, ref=ref)
+
+
 def pack_masks(bits: np.ndarray) -> np.ndarray:
     """bool [B][n_items] -> uint64 [B][ceil(n_items/64)], bit i of word i//64 = item i."""
     B, n = bits.shape
@@ -538,13 +629,14 @@ def solve(shape: DecoderShape, layers, kv, x0: np.ndarray, ctx: int, latency: di
           n_budgets: int, gamma: Sequence[int], tau: float = -np.inf, skip_cap: int = -1,
           per_item: Optional[Sequence[float]] = None, cache_widened: bool = False,
           apply_item: Optional[Callable] = None,
-          w_lm: Optional[np.ndarray] = None) -> SolveResult:
+          w_lm: Optional[np.ndarray] = None, beam: int = 1) -> SolveResult:
     """Latencies -> weights -> DP -> per-budget draft latency -> TPT grid, for one sequence.
 
     t_Draft(S) = fixed + sum_{i in S} t_i and t_Target = fixed + sum_i t_i: one draft pass
     runs the kept items, one verification pass runs all of them (readings; the page defines
     TPT in terms of both but prints no formula for them).  x0 is [d] (one token) or [r][d]
     (an r-token window).  With ``w_lm`` the TPT grid uses alpha_lm_head, else clamp(cos).
+    ``beam`` > 1 runs knapsack_dp_beam and uses each budget's best set.
     """
     n_items = 2 * shape.n_layers
     t = item_latencies(shape.n_layers, ctx, latency["attn_base"], latency["attn_per_token"],
@@ -552,7 +644,10 @@ def solve(shape: DecoderShape, layers, kv, x0: np.ndarray, ctx: int, latency: di
     w = item_weights(t, n_budgets)
     fn = apply_item if apply_item is not None else DecoderItems(shape, layers, kv, ctx,
                                                                  cache_widened)
-    dp = knapsack_dp(fn, n_items, w, x0, n_budgets, tau, skip_cap)
+    if beam > 1:
+        dp = knapsack_dp_beam(fn, n_items, w, x0, n_budgets, beam, tau, skip_cap).best()
+    else:
+        dp = knapsack_dp(fn, n_items, w, x0, n_budgets, tau, skip_cap)
     fixed = float(latency.get("fixed", 0.0))
     t_draft = np.array([fixed + float(np.sum(t[dp.bits[b]])) for b in range(n_budgets)])
     t_target = fixed + float(np.sum(t))
