@@ -17,7 +17,8 @@ enum ActType : int { ACT_F32 = 0, ACT_BF16 = 1 };
 // ---------------------------------------------------------------------------------------
 enum GemmMode : int { GEMM_PARTIAL = 0, GEMM_SWIGLU = 1 };
 
-constexpr int WIN_MAX = 8;  // largest window r (tokens per DP state)
+constexpr int WIN_MAX = 8;   // largest window r (tokens per DP state)
+constexpr int BEAM_MAX = 8;  // largest beam width (states kept per DP cell)
 
 struct GemmArgs {
   const void* A;  // [R][lda] activations (bf16 or f32, same as W)
@@ -137,11 +138,14 @@ struct ReduceArgs {
 
 struct SelectArgs {
   int item, n_items, B, Bm, d, mw, n_seqs;
-  int wmax;                // state rows per budget slot (window capacity)
+  int wmax;                // state rows per beam slot (window capacity)
   int rmax;                // largest window r among the solve's sequences
+  int kmax;                // beam slots per budget (capacity); valid, masks, exec_row and
+                           // next_row hold kmax entries per budget, slot 0 first
+  int beam;                // beam width k of this solve (1: the one-state DP)
   const float* E;          // [Rtot][d] item outputs incl. residual (ReduceArgs::E)
   int Rtot;
-  const float* state_old;  // [S][Bm+1][wmax][d], budget index Bm = reference
+  const float* state_old;  // [S][Bm+1][kmax][wmax][d], budget index Bm = reference (slot 0)
   float* state_new;
   const uint8_t* valid_old;  // [S][Bm]
   uint8_t* valid_new;
@@ -161,11 +165,11 @@ struct SelectArgs {
 };
 
 struct InitArgs {
-  int n_seqs, Bm, d, mw, wmax;
+  int n_seqs, Bm, d, mw, wmax, kmax;
   const float* const* x0;  // device array [n_seqs] of device pointers to [r][d]
-  float* state;            // [S][Bm+1][wmax][d]
-  uint8_t* valid;          // [S][Bm]
-  uint64_t* masks;         // [S][Bm][mw]
+  float* state;            // [S][Bm+1][kmax][wmax][d]
+  uint8_t* valid;          // [S][Bm][kmax]
+  uint64_t* masks;         // [S][Bm][kmax][mw]
   const int* rows;         // [S][4]: first row of budget 0 and of the reference in item 0
                            // (-1 none), the window r, unused
   void* xa;                // item 0 activations

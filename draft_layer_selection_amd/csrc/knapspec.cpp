@@ -64,11 +64,11 @@ struct MapLayout {
 };
 
 MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int hkv, int G,
-                     int dh, int asplit_max, size_t wmax) {
+                     int dh, int asplit_max, size_t wmax, size_t kmax) {
   MapLayout L{};
   Carver c;
-  L.exec = c.take((size_t)L2 * S * Bm * 4);
-  L.next = c.take((size_t)L2 * S * Bm * 4);
+  L.exec = c.take((size_t)L2 * S * Bm * kmax * 4);
+  L.next = c.take((size_t)L2 * S * Bm * kmax * 4);
   L.rowseq = c.take((size_t)L2 * Rmax * 4);
   L.rowstate = c.take((size_t)L2 * Rmax * 4);
   L.rowtok = c.take((size_t)L2 * Rmax * 4);
@@ -79,7 +79,7 @@ MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int
   L.init = c.take(S * 4 * 4);
   // per layer: every (sequence, KV head, query block, split) once, plus the empty entries
   // that keep each die's share of the list aligned (at most one query-block group per die)
-  const size_t qb_max = (G * (Bm + 1) * wmax + 63) / 64;
+  const size_t qb_max = (G * (Bm + 1) * wmax * kmax + 63) / 64;
   L.max_work = (size_t)n_layers * (S * hkv * qb_max * asplit_max + N_XCD * qb_max);
   L.work = c.take(L.max_work * 16);
   L.total = c.off;
@@ -148,6 +148,7 @@ struct knapspec_model {
   // dimensions
   int L2 = 0, mw = 0, qdim = 0, kvdim = 0, nqkv = 0, Rmax = 0;
   int wmax = 1;  // tokens per state slot (largest window)
+  int kmax = 1;  // beam slots per budget (largest beam)
   size_t p_floats = 0;
   size_t part_slots = 0;  // attention partial results: (split, row, query head) slots
   int n_cus = 0;
@@ -376,6 +377,8 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   if (d.max_ctx < 0) return fail(KNAPSPEC_EINVAL, "max_ctx must be >= 0");
   if (d.max_window < 0 || d.max_window > KNAPSPEC_WINDOW_MAX)
     return fail(KNAPSPEC_EINVAL, "max_window must be in [0, %d]", KNAPSPEC_WINDOW_MAX);
+  if (d.max_beam < 0 || d.max_beam > KNAPSPEC_BEAM_MAX)
+    return fail(KNAPSPEC_EINVAL, "max_beam must be in [0, %d]", KNAPSPEC_BEAM_MAX);
   if (!(d.rms_eps > 0.f) || !std::isfinite(d.rms_eps))
     return fail(KNAPSPEC_EINVAL, "rms_eps must be finite and > 0");
   if (!(d.rope_theta > 0.f) || !std::isfinite(d.rope_theta))
@@ -430,18 +433,19 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   m->nqkv = m->qdim + 2 * m->kvdim;
   const size_t S = d.max_seqs, Bm = d.max_budgets, D = d.d_model;
   m->wmax = std::max(1, (int)d.max_window);
-  const size_t Wm = m->wmax;
-  // rows of one item: per sequence (live sources + reference) x window; the acceptance
+  m->kmax = std::max(1, (int)d.max_beam);
+  const size_t Wm = m->wmax, Kb = m->kmax;
+  // rows of one item: per sequence (live source slots + reference) x window; the acceptance
   // estimate's LM-head pass uses (budgets + reference) x window rows
-  m->Rmax = (int)(S * (Bm + 1) * Wm);
+  m->Rmax = (int)(S * (Bm + 1) * Kb * Wm);
   const size_t R = m->Rmax;
   const size_t nmax = std::max<size_t>(m->nqkv, D);
   m->p_floats = std::max<size_t>(PSPLIT_MAX * std::min<size_t>(R, 256), R) * nmax;
 
   Carver c;
-  const size_t o_state = c.take(2 * S * (Bm + 1) * Wm * D * 4);
-  const size_t o_valid = c.take(2 * S * Bm);
-  const size_t o_masks = c.take(2 * S * Bm * m->mw * 8);
+  const size_t o_state = c.take(2 * S * (Bm + 1) * Kb * Wm * D * 4);
+  const size_t o_valid = c.take(2 * S * Bm * Kb);
+  const size_t o_masks = c.take(2 * S * Bm * Kb * m->mw * 8);
   const size_t o_xa = c.take(R * D * m->elem);
   const size_t o_q = c.take(R * m->qdim * m->elem);
   const size_t o_ks = c.take(R * m->kvdim * 4);
@@ -460,7 +464,7 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   // row maps and launch tables, rebuilt on the host each solve and uploaded once
   const int G = d.n_q_heads / d.n_kv_heads;
   m->maps_bytes = map_layout(m->L2, d.n_layers, S, Bm, R, d.n_kv_heads, G, d.head_dim,
-                             ASPLIT_MAX, Wm).total;
+                             ASPLIT_MAX, Wm, Kb).total;
   const size_t o_maps = c.take(m->maps_bytes);
   m->ws_bytes = c.off;
 
@@ -471,7 +475,8 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
     delete m;
     return fail(KNAPSPEC_ENOMEM, "device workspace allocation of %zu bytes failed", need);
   }
-  m->h_out_bytes = align_up(S * Bm * m->mw * 8) + align_up(S * Bm * 4) + align_up(S * Bm) +
+  m->h_out_bytes = align_up(S * Bm * Kb * m->mw * 8) + align_up(S * Bm * 4) +
+                   align_up(S * Bm * Kb) +
                    align_up(S * m->L2 * Bm) + align_up(S * m->L2 * Bm * 4) +
                    align_up(S * (Bm + 1) * Wm * 4);
   if (hipHostMalloc((void**)&m->h_maps, m->maps_bytes, hipHostMallocDefault) != hipSuccess ||
@@ -488,11 +493,11 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   }
   char* ws = m->ws;
   m->state[0] = (float*)(ws + o_state);
-  m->state[1] = m->state[0] + S * (Bm + 1) * Wm * D;
+  m->state[1] = m->state[0] + S * (Bm + 1) * Kb * Wm * D;
   m->valid[0] = (uint8_t*)(ws + o_valid);
-  m->valid[1] = m->valid[0] + S * Bm;
+  m->valid[1] = m->valid[0] + S * Bm * Kb;
   m->masks[0] = (uint64_t*)(ws + o_masks);
-  m->masks[1] = m->masks[0] + S * Bm * m->mw;
+  m->masks[1] = m->masks[0] + S * Bm * Kb * m->mw;
   m->xa = ws + o_xa;
   m->q = ws + o_q;
   m->kself = (float*)(ws + o_ks);
@@ -618,7 +623,7 @@ struct SeqPlan {
   std::vector<double> t;
   std::vector<int32_t> w;
   std::vector<int> prefix;
-  // src[i] = sorted source budgets of item i
+  // src[i] = source slots of item i as budget * kmax + beam slot, by budget then slot
   std::vector<std::vector<int>> src;
 };
 
@@ -645,6 +650,11 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   if ((args->flags & KNAPSPEC_RETURN_MARGINS) && !res->margins)
     return fail(KNAPSPEC_EINVAL, "KNAPSPEC_RETURN_MARGINS set but result.margins is NULL");
   const bool use_lm = (args->flags & KNAPSPEC_ALPHA_LM_HEAD) != 0;
+  const int K = std::max(1, (int)args->beam);
+  if (args->beam < 0 || K > m->kmax)
+    return fail(KNAPSPEC_EINVAL, "beam must be in [0, %d] (model max_beam)", m->kmax);
+  if (K > 1 && (args->flags & (KNAPSPEC_RETURN_DECISIONS | KNAPSPEC_RETURN_MARGINS)))
+    return fail(KNAPSPEC_EINVAL, "per-cell decisions and margins need beam <= 1");
   if (use_lm && !m->lm_w)
     return fail(KNAPSPEC_EINVAL, "KNAPSPEC_ALPHA_LM_HEAD set but no LM head (knapspec_set_lm_head)");
   for (int q = 0; q < S; ++q) {
@@ -670,7 +680,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
 
   const int L2 = m->L2, Bm = d.max_budgets, D = d.d_model, mw = m->mw;
   const int hq = d.n_q_heads, hkv = d.n_kv_heads, dh = d.head_dim, G = hq / hkv;
-  const int Wm = m->wmax;
+  const int Wm = m->wmax, Kb = m->kmax;
   // window r of each sequence; rows of its LM-head pass start at lm_off[q]
   std::vector<int> win(S), lm_off(S);
   int rmax = 1, Rlm = 0;
@@ -692,16 +702,19 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     if (rc) return rc;
     p.prefix.resize(L2);
     p.src.resize(L2);
-    std::vector<uint8_t> reach(B, 0);
-    reach[0] = 1;
+    // states per budget before item i (distinct subsets of that weight, capped at the beam;
+    // 0/1 = reachability for the one-state DP)
+    std::vector<int> cnt(B, 0), nxt(B);
+    cnt[0] = 1;
     int pre = 0;
     for (int i = 0; i < L2; ++i) {
       const int w = p.w[i];
       pre += w;
       p.prefix[i] = pre;
       for (int s = 0; s + w <= B - 1; ++s)
-        if (reach[s]) p.src[i].push_back(s);
-      for (int s : p.src[i]) reach[s + w] = 1;
+        for (int j = 0; j < cnt[s]; ++j) p.src[i].push_back(s * Kb + j);
+      for (int b = 0; b < B; ++b) nxt[b] = std::min(K, cnt[b] + (b >= w ? cnt[b - w] : 0));
+      cnt.swap(nxt);
     }
   }
   // rows of each item: per sequence [sources..., reference], each a group of r token rows
@@ -717,7 +730,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   }
 
   // ---- build the map/launch tables in pinned host memory
-  const MapLayout ml = map_layout(L2, d.n_layers, S, Bm, m->Rmax, hkv, G, dh, ASPLIT_MAX, Wm);
+  const MapLayout ml = map_layout(L2, d.n_layers, S, Bm, m->Rmax, hkv, G, dh, ASPLIT_MAX, Wm,
+                                  Kb);
   const size_t o_exec = ml.exec, o_next = ml.next, o_rowseq = ml.rowseq,
                o_rowstate = ml.rowstate, o_rowtok = ml.rowtok, o_info = ml.info,
                o_work = ml.work, o_aseq = ml.aseq, o_rope = ml.rope, o_x0 = ml.x0,
@@ -737,8 +751,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   const float** x0p = (const float**)(hm + o_x0);
   int32_t* init_rows = (int32_t*)(hm + o_init);
 
-  std::fill(exec_row, exec_row + (size_t)L2 * S * Bm, -1);
-  std::fill(next_row, next_row + (size_t)L2 * S * Bm, -1);
+  std::fill(exec_row, exec_row + (size_t)L2 * S * Bm * Kb, -1);
+  std::fill(next_row, next_row + (size_t)L2 * S * Bm * Kb, -1);
   for (int i = 0; i < L2; ++i) {
     for (int q = 0; q < S; ++q) {
       const SeqPlan& p = plan[q];
@@ -751,11 +765,12 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
           row_seq[row] = q;
           // state row the item is applied to: token t of a source budget or of the reference
           // (budget index Bm) in the [S][Bm+1][wmax] slot layout
-          row_state[row] = (q * (Bm + 1) + (j + 1 < ng ? p.src[i][j] : Bm)) * Wm + t;
+          const int slot = j + 1 < ng ? p.src[i][j] : Bm * Kb;  // budget * kmax + beam slot
+          row_state[row] = ((q * (Bm + 1)) * Kb + slot) * Wm + t;
           row_tok[row] = t;
         }
-      int32_t* er = exec_row + ((size_t)i * S + q) * Bm;
-      for (int j = 0; j + 1 < ng; ++j) er[p.src[i][j] + p.w[i]] = off + j * wr;
+      int32_t* er = exec_row + ((size_t)i * S + q) * Bm * Kb;
+      for (int j = 0; j + 1 < ng; ++j) er[p.src[i][j] + p.w[i] * Kb] = off + j * wr;
       ks::ItemSeq& in = info[(size_t)i * S + q];
       in.w = p.w[i];
       in.prefix = p.prefix[i];
@@ -765,7 +780,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
       in.next_ref_row = -1;
       in.win = wr;
       in.pad1 = 0;
-      int32_t* nr = next_row + ((size_t)i * S + q) * Bm;
+      int32_t* nr = next_row + ((size_t)i * S + q) * Bm * Kb;
       if (i + 1 < L2) {
         const int noff = row_off[(size_t)(i + 1) * S + q];
         const int nng = (int)p.src[i + 1].size() + 1;
@@ -773,7 +788,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
         in.next_ref_row = noff + (nng - 1) * wr;
       } else if (use_lm) {
         // the final states' RMSNorm'd rows feed the LM-head pass: budget b, then the reference
-        for (int b = 0; b < B; ++b) nr[b] = lm_off[q] + b * wr;
+        for (int b = 0; b < B; ++b) nr[(size_t)b * Kb] = lm_off[q] + b * wr;  // best slot
         in.next_ref_row = lm_off[q] + B * wr;
       }
     }
@@ -864,9 +879,9 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   // ---- output staging layout (pinned host)
   char* ho = m->h_out;
   Carver oc;
-  const size_t ho_masks = oc.take((size_t)S * Bm * mw * 8);
+  const size_t ho_masks = oc.take((size_t)S * Bm * Kb * mw * 8);
   const size_t ho_cos = oc.take((size_t)S * Bm * 4);
-  const size_t ho_valid = oc.take((size_t)S * Bm);
+  const size_t ho_valid = oc.take((size_t)S * Bm * Kb);
   const size_t ho_dec = oc.take((size_t)S * L2 * Bm);
   const size_t ho_mar = oc.take((size_t)S * L2 * Bm * 4);
   const size_t ho_tok = oc.take((size_t)S * (Bm + 1) * Wm * 4);
@@ -896,6 +911,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     ia.d = D;
     ia.mw = mw;
     ia.wmax = Wm;
+    ia.kmax = Kb;
     ia.x0 = (const float* const*)(dm + o_x0);
     ia.state = m->state[0];
     ia.valid = m->valid[0];
@@ -1035,6 +1051,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     sa.n_seqs = S;
     sa.wmax = Wm;
     sa.rmax = rmax;
+    sa.kmax = Kb;
+    sa.beam = K;
     sa.E = m->E;
     sa.Rtot = R;
     sa.state_old = m->state[cur];
@@ -1043,8 +1061,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     sa.valid_new = m->valid[cur ^ 1];
     sa.mask_old = m->masks[cur];
     sa.mask_new = m->masks[cur ^ 1];
-    sa.exec_row = d_exec + (size_t)i * S * Bm;
-    sa.next_row = d_next + (size_t)i * S * Bm;
+    sa.exec_row = d_exec + (size_t)i * S * Bm * Kb;
+    sa.next_row = d_next + (size_t)i * S * Bm * Kb;
     sa.info = d_info + (size_t)i * S;
     sa.tau = args->tau;
     sa.skip_cap = args->max_skip_weight;
@@ -1089,10 +1107,11 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   }
 
   // ---- results back to the host
-  HIPCHK(hipMemcpyAsync(ho + ho_masks, m->masks[cur], (size_t)S * Bm * mw * 8,
+  HIPCHK(hipMemcpyAsync(ho + ho_masks, m->masks[cur], (size_t)S * Bm * Kb * mw * 8,
                         hipMemcpyDeviceToHost, st));
   HIPCHK(hipMemcpyAsync(ho + ho_cos, m->cos, (size_t)S * Bm * 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(hipMemcpyAsync(ho + ho_valid, m->valid[cur], (size_t)S * Bm, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipMemcpyAsync(ho + ho_valid, m->valid[cur], (size_t)S * Bm * Kb, hipMemcpyDeviceToHost,
+                        st));
   if (want_dec)
     HIPCHK(hipMemcpyAsync(ho + ho_dec, m->decisions, (size_t)S * L2 * Bm, hipMemcpyDeviceToHost, st));
   if (want_mar)
@@ -1120,6 +1139,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     std::memcpy(&tau_bits, &args->tau, 4);
     key.insert(key.end(), {S, B, tau_bits, args->max_skip_weight, args->flags});
     if (use_lm) key.insert(key.end(), {(int64_t)(intptr_t)m->lm_w, m->lm_vocab});
+    key.push_back(K);
     for (int q = 0; q < S; ++q) {
       key.push_back(args->seqs[q].ctx_len);
       key.push_back(win[q]);
@@ -1169,9 +1189,10 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   for (int q = 0; q < S; ++q) {
     const SeqPlan& p = plan[q];
     for (int b = 0; b < B; ++b) {
-      const size_t src = (size_t)q * Bm + b, dst = (size_t)q * B + b;
+      // each budget's best set: beam slot 0
+      const size_t src = ((size_t)q * Bm + b) * Kb, dst = (size_t)q * B + b;
       std::memcpy(res->masks + dst * mw, hmask + src * mw, (size_t)mw * 8);
-      res->cos[dst] = hvalid[src] ? hcos[src] : std::numeric_limits<float>::quiet_NaN();
+      res->cos[dst] = hvalid[src] ? hcos[(size_t)q * Bm + b] : std::numeric_limits<float>::quiet_NaN();
       res->valid[dst] = hvalid[src];
       double td = fixed;
       for (int i = 0; i < L2; ++i)
@@ -1403,6 +1424,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
     ia.d = D;
     ia.mw = m->mw;
     ia.wmax = m->wmax;
+    ia.kmax = m->kmax;
     ia.x0 = (const float* const*)(dp + o_x0);
     ia.state = m->state[0];
     ia.valid = m->valid[0];

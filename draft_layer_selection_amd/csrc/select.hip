@@ -73,7 +73,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   const bool is_ref = b == a.B;
   const ItemSeq inf = a.info[q];
   const int d4 = a.d / 4;
-  const size_t slot = (size_t)a.wmax * a.d;  // floats per budget slot (token 0 used)
+  const size_t slot = (size_t)a.kmax * a.wmax * a.d;  // floats per budget slot (token 0 used)
   const size_t sstride = (size_t)(a.Bm + 1) * slot;  // per-sequence state stride
   const float* st_old = a.state_old + q * sstride;
   float* st_new = a.state_new + q * sstride;
@@ -98,10 +98,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   }
 
   const int qb = q * a.Bm + b;
-  const int erow = a.exec_row[qb];
+  const int erow = a.exec_row[(size_t)qb * a.kmax];
   const int src = b - inf.w;
-  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
-  const bool has_skip = a.valid_old[qb] != 0;
+  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[(size_t)(q * a.Bm + src) * a.kmax];
+  const bool has_skip = a.valid_old[(size_t)qb * a.kmax] != 0;
   const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;
   const float* g_row = st_old + (size_t)b * slot;
 
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   if (a.skip_cap >= 0 && inf.prefix - b > a.skip_cap) alive = false;
 
   if (threadIdx.x == 0) {
-    a.valid_new[qb] = alive ? 1 : 0;
+    a.valid_new[(size_t)qb * a.kmax] = alive ? 1 : 0;
     const size_t cell = ((size_t)q * a.n_items + a.item) * a.Bm + b;
     if (a.decisions) a.decisions[cell] = alive ? (take ? 1 : 0) : 255;
     if (a.margins) {
@@ -147,17 +147,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
     uint64_t mval = 0;
     if (alive) {
       if (take) {
-        mval = a.mask_old[((size_t)q * a.Bm + src) * a.mw + wd];
+        mval = a.mask_old[((size_t)q * a.Bm + src) * a.kmax * a.mw + wd];
         if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
       } else {
-        mval = a.mask_old[(size_t)qb * a.mw + wd];
+        mval = a.mask_old[(size_t)qb * a.kmax * a.mw + wd];
       }
     }
-    a.mask_new[(size_t)qb * a.mw + wd] = mval;
+    a.mask_new[(size_t)qb * a.kmax * a.mw + wd] = mval;
   }
 
   // pass 2: kept state and its RMSNorm'd activation row for the next item
-  const int nrow = a.next_row[qb];
+  const int nrow = a.next_row[(size_t)qb * a.kmax];
   if (!alive) {
     if (nrow >= 0) {
       for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   const bool is_ref = b == a.B;
   const ItemSeq inf = a.info[q];
   const int d4 = a.d / 4;
-  const size_t slot = (size_t)a.wmax * a.d;  // floats per budget slot
+  const size_t slot = (size_t)a.kmax * a.wmax * a.d;  // floats per budget slot
   const size_t sstride = (size_t)(a.Bm + 1) * slot;
   const float* st_old = a.state_old + q * sstride;
   float* st_new = a.state_new + q * sstride;
@@ -219,10 +219,10 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   }
 
   const int qb = q * a.Bm + b;
-  const int erow = a.exec_row[qb];
+  const int erow = a.exec_row[(size_t)qb * a.kmax];
   const int src = b - inf.w;
-  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
-  const bool has_skip = a.valid_old[qb] != 0;
+  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[(size_t)(q * a.Bm + src) * a.kmax];
+  const bool has_skip = a.valid_old[(size_t)qb * a.kmax] != 0;
   const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;
   const float* g_row = st_old + (size_t)b * slot;
 
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   if (a.skip_cap >= 0 && inf.prefix - b > a.skip_cap) alive = false;
 
   if (threadIdx.x == 0) {
-    a.valid_new[qb] = alive ? 1 : 0;
+    a.valid_new[(size_t)qb * a.kmax] = alive ? 1 : 0;
     const size_t cell = ((size_t)q * a.n_items + a.item) * a.Bm + b;
     if (a.decisions) a.decisions[cell] = alive ? (take ? 1 : 0) : 255;
     if (a.margins) {
@@ -265,16 +265,16 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
     uint64_t mval = 0;
     if (alive) {
       if (take) {
-        mval = a.mask_old[((size_t)q * a.Bm + src) * a.mw + wd];
+        mval = a.mask_old[((size_t)q * a.Bm + src) * a.kmax * a.mw + wd];
         if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
       } else {
-        mval = a.mask_old[(size_t)qb * a.mw + wd];
+        mval = a.mask_old[(size_t)qb * a.kmax * a.mw + wd];
       }
     }
-    a.mask_new[(size_t)qb * a.mw + wd] = mval;
+    a.mask_new[(size_t)qb * a.kmax * a.mw + wd] = mval;
   }
 
-  const int nrow = a.next_row[qb];
+  const int nrow = a.next_row[(size_t)qb * a.kmax];
   const float ms = (take ? acc[2] : acc[4]) / (float)a.d;
   const float scale = alive ? 1.0f / sqrtf(ms + a.eps) : 0.f;
   float* out = st_new + (size_t)b * slot;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(SELW_THREADS) void select_win_kernel(SelectArgs a) 
   const ItemSeq inf = a.info[q];
   const int r = inf.win;
   const int d4 = a.d / 4;
-  const size_t slot = (size_t)a.wmax * a.d;
+  const size_t slot = (size_t)a.kmax * a.wmax * a.d;
   const size_t sstride = (size_t)(a.Bm + 1) * slot;
   const float* st_old = a.state_old + q * sstride;
   float* st_new = a.state_new + q * sstride;
@@ -338,10 +338,10 @@ __global__ __launch_bounds__(SELW_THREADS) void select_win_kernel(SelectArgs a) 
   }
 
   const int qb = q * a.Bm + b;
-  const int erow = a.exec_row[qb];
+  const int erow = a.exec_row[(size_t)qb * a.kmax];
   const int src = b - inf.w;
-  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[q * a.Bm + src];
-  const bool has_skip = a.valid_old[qb] != 0;
+  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[(size_t)(q * a.Bm + src) * a.kmax];
+  const bool has_skip = a.valid_old[(size_t)qb * a.kmax] != 0;
   const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;  // r consecutive rows
   const float* g_row = st_old + (size_t)b * slot;                    // r rows of the slot
 
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(SELW_THREADS) void select_win_kernel(SelectArgs a) 
   if (a.skip_cap >= 0 && inf.prefix - b > a.skip_cap) alive = false;
 
   if (threadIdx.x == 0) {
-    a.valid_new[qb] = alive ? 1 : 0;
+    a.valid_new[(size_t)qb * a.kmax] = alive ? 1 : 0;
     const size_t cell = ((size_t)q * a.n_items + a.item) * a.Bm + b;
     if (a.decisions) a.decisions[cell] = alive ? (take ? 1 : 0) : 255;
     if (a.margins) {
@@ -397,16 +397,16 @@ __global__ __launch_bounds__(SELW_THREADS) void select_win_kernel(SelectArgs a) 
     uint64_t mval = 0;
     if (alive) {
       if (take) {
-        mval = a.mask_old[((size_t)q * a.Bm + src) * a.mw + wd];
+        mval = a.mask_old[((size_t)q * a.Bm + src) * a.kmax * a.mw + wd];
         if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
       } else {
-        mval = a.mask_old[(size_t)qb * a.mw + wd];
+        mval = a.mask_old[(size_t)qb * a.kmax * a.mw + wd];
       }
     }
-    a.mask_new[(size_t)qb * a.mw + wd] = mval;
+    a.mask_new[(size_t)qb * a.kmax * a.mw + wd] = mval;
   }
 
-  const int nrow = a.next_row[qb];
+  const int nrow = a.next_row[(size_t)qb * a.kmax];
   float* out = st_new + (size_t)b * slot;
 #pragma unroll
   for (int t = 0; t < WIN_MAX; ++t) {
@@ -419,6 +419,180 @@ __global__ __launch_bounds__(SELW_THREADS) void select_win_kernel(SelectArgs a) 
       const f32x4 x = alive ? *(const f32x4*)(xr + 4 * e4) : zero;
       if (alive) *(f32x4*)(out + (size_t)t * a.d + 4 * e4) = x;
       if (nrow >= 0) store_act<T>(a.xa_next, nrow + t, a.d, e4, x, scale);
+    }
+  }
+}
+
+// Select of the beam variant (beam k = SelectArgs::beam in 2..BEAM_MAX, any window r): the
+// candidates of budget b are its k skip states (slots of b) and the item applied to the k
+// states of b - w (rows of this item); each is scored by the cosine of its flattened r x d
+// state with the reference, ranked higher first with ties to the lower candidate index
+// (skip slots 0..k-1, then execute slots 0..k-1), NaN as -inf; the first k valid candidates
+// that pass tau and the skip cap become slots 0..k-1.  Kept rows get per-token RMSNorm scales
+// for the next item's activations.
+constexpr int SELB_THREADS = 512;
+constexpr int SELB_SUMS = 1 + 4 * BEAM_MAX;  // rr, then (dot, norm^2) of 2k candidates
+
+template <class T>
+__global__ __launch_bounds__(SELB_THREADS) void select_beam_kernel(SelectArgs a) {
+  const int q = blockIdx.x / (a.B + 1);
+  const int b = blockIdx.x % (a.B + 1);
+  const bool is_ref = b == a.B;
+  const ItemSeq inf = a.info[q];
+  const int r = inf.win, K = a.beam;
+  const int d4 = a.d / 4;
+  const size_t bslot = (size_t)a.wmax * a.d;     // floats per beam slot
+  const size_t bstride = (size_t)a.kmax * bslot;  // floats per budget
+  const size_t sstride = (size_t)(a.Bm + 1) * bstride;
+  const float* st_old = a.state_old + q * sstride;
+  float* st_new = a.state_new + q * sstride;
+  const float* ref = a.E + (size_t)inf.ref_row * a.d;
+  __shared__ float scratch[SELB_SUMS * (SELB_THREADS / 64)];
+  __shared__ int keep[BEAM_MAX];
+
+  if (is_ref) {
+    float ss[WIN_MAX];
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) {
+      if (t >= r) continue;
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SELB_THREADS) {
+        const f32x4 x = *(const f32x4*)(ref + (size_t)t * a.d + 4 * e4);
+        *(f32x4*)(st_new + (size_t)a.Bm * bstride + (size_t)t * a.d + 4 * e4) = x;
+        ss[t] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      }
+    }
+    if (inf.next_ref_row < 0) return;
+    block_sum<WIN_MAX, SELB_THREADS>(ss, scratch);
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) {
+      if (t >= r) continue;
+      const float scale = 1.0f / sqrtf(ss[t] / (float)a.d + a.eps);
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SELB_THREADS) {
+        const f32x4 x =
+            *(const f32x4*)(st_new + (size_t)a.Bm * bstride + (size_t)t * a.d + 4 * e4);
+        store_act<T>(a.xa_next, inf.next_ref_row + t, a.d, e4, x, scale);
+      }
+    }
+    return;
+  }
+
+  const size_t qbk = ((size_t)q * a.Bm + b) * a.kmax;       // first slot entry of budget b
+  const int src = b - inf.w;
+  const size_t sbk = ((size_t)q * a.Bm + (src >= 0 ? src : 0)) * a.kmax;
+  // candidate c: c < K skip state of slot c; K <= c < 2K item output of source slot c - K
+  auto cand_row = [&](int c) -> const float* {
+    if (c < K) return st_old + (size_t)b * bstride + (size_t)c * bslot;
+    return a.E + (size_t)a.exec_row[qbk + (c - K)] * a.d;
+  };
+  bool has[2 * BEAM_MAX];
+#pragma unroll
+  for (int c = 0; c < 2 * BEAM_MAX; ++c) {
+    has[c] = false;
+    if (c < K) {
+      has[c] = a.valid_old[qbk + c] != 0;
+    } else if (c < 2 * K) {
+      const int j = c - K;
+      has[c] = a.exec_row[qbk + j] >= 0 && src >= 0 && a.valid_old[sbk + j] != 0;
+    }
+  }
+  float acc[SELB_SUMS];
+#pragma unroll
+  for (int i = 0; i < SELB_SUMS; ++i) acc[i] = 0.f;
+  for (int t = 0; t < r; ++t) {
+    for (int e4 = threadIdx.x; e4 < d4; e4 += SELB_THREADS) {
+      const size_t o = (size_t)t * a.d + 4 * e4;
+      const f32x4 rv = *(const f32x4*)(ref + o);
+      acc[0] += rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2] + rv[3] * rv[3];
+#pragma unroll
+      for (int c = 0; c < 2 * BEAM_MAX; ++c) {
+        if (!has[c]) continue;
+        const f32x4 x = *(const f32x4*)(cand_row(c) + o);
+        acc[1 + 2 * c] += x[0] * rv[0] + x[1] * rv[1] + x[2] * rv[2] + x[3] * rv[3];
+        acc[2 + 2 * c] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      }
+    }
+  }
+  block_sum<SELB_SUMS, SELB_THREADS>(acc, scratch);
+  if (threadIdx.x == 0) {
+    float cs[2 * BEAM_MAX];
+    int order[2 * BEAM_MAX];
+    int n = 0;
+    for (int c = 0; c < 2 * K; ++c) {
+      cs[c] = has[c] ? nan_to_ninf(acc[1 + 2 * c] / (sqrtf(acc[2 + 2 * c]) * sqrtf(acc[0])))
+                     : -INFINITY;
+      // insertion by (cosine descending, candidate index ascending)
+      int p = n++;
+      while (p > 0 && cs[order[p - 1]] < cs[c]) {
+        order[p] = order[p - 1];
+        --p;
+      }
+      order[p] = c;
+    }
+    const bool capped = a.skip_cap >= 0 && inf.prefix - b > a.skip_cap;
+    int kept = 0;
+    for (int m = 0; m < n && kept < K && !capped; ++m) {
+      const int c = order[m];
+      if (!(cs[c] > -INFINITY) || cs[c] < a.tau) break;
+      keep[kept++] = c;
+    }
+    for (int j = kept; j < K; ++j) keep[j] = -1;
+    if (a.item == a.n_items - 1) a.cos_out[q * a.Bm + b] = kept ? cs[keep[0]] : NAN;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.kmax; j += SELB_THREADS)
+    a.valid_new[qbk + j] = (j < K && keep[j] >= 0) ? 1 : 0;
+  for (int idx = threadIdx.x; idx < K * a.mw; idx += SELB_THREADS) {
+    const int j = idx / a.mw, wd = idx % a.mw;
+    const int c = keep[j];
+    uint64_t mval = 0;
+    if (c >= 0 && c < K) {
+      mval = a.mask_old[(qbk + c) * a.mw + wd];
+    } else if (c >= K) {
+      mval = a.mask_old[(sbk + (c - K)) * a.mw + wd];
+      if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
+    }
+    a.mask_new[(qbk + j) * a.mw + wd] = mval;
+  }
+  // kept states and their RMSNorm'd rows for the next item
+  for (int j = 0; j < K; ++j) {
+    const int c = keep[j];
+    const int nrow = a.next_row[qbk + j];
+    if (c < 0) {
+      if (nrow >= 0) {
+        for (int t = 0; t < r; ++t)
+          for (int e4 = threadIdx.x; e4 < d4; e4 += SELB_THREADS) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            store_act<T>(a.xa_next, nrow + t, a.d, e4, z, 0.f);
+          }
+      }
+      continue;
+    }
+    const float* xr = cand_row(c);
+    float* out = st_new + (size_t)b * bstride + (size_t)j * bslot;
+    float ss[WIN_MAX];
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) {
+      if (t >= r) continue;
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SELB_THREADS) {
+        const f32x4 x = *(const f32x4*)(xr + (size_t)t * a.d + 4 * e4);
+        *(f32x4*)(out + (size_t)t * a.d + 4 * e4) = x;
+        ss[t] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      }
+    }
+    if (nrow < 0) continue;
+    block_sum<WIN_MAX, SELB_THREADS>(ss, scratch);
+#pragma unroll
+    for (int t = 0; t < WIN_MAX; ++t) {
+      if (t >= r) continue;
+      const float scale = 1.0f / sqrtf(ss[t] / (float)a.d + a.eps);
+      for (int e4 = threadIdx.x; e4 < d4; e4 += SELB_THREADS) {
+        const f32x4 x = *(const f32x4*)(xr + (size_t)t * a.d + 4 * e4);
+        store_act<T>(a.xa_next, nrow + t, a.d, e4, x, scale);
+      }
     }
   }
 }
@@ -466,12 +640,14 @@ __global__ __launch_bounds__(SEL_THREADS) void init_kernel(InitArgs a) {
   const int q = blockIdx.x;
   const float* x0 = a.x0[q];  // [r][d]
   const int r0 = a.rows[4 * q], rref = a.rows[4 * q + 1], win = a.rows[4 * q + 2];
-  const size_t slot = (size_t)a.wmax * a.d;
+  const size_t slot = (size_t)a.kmax * a.wmax * a.d;
   const size_t sstride = (size_t)(a.Bm + 1) * slot;
   float* st = a.state + q * sstride;
-  for (int b = threadIdx.x; b < a.Bm; b += SEL_THREADS) a.valid[q * a.Bm + b] = b == 0 ? 1 : 0;
-  for (int i = threadIdx.x; i < a.Bm * a.mw; i += SEL_THREADS)
-    a.masks[(size_t)q * a.Bm * a.mw + i] = 0;
+  const int nslots = a.Bm * a.kmax;  // (budget, beam slot) pairs; slot (0, 0) holds x0
+  for (int i = threadIdx.x; i < nslots; i += SEL_THREADS)
+    a.valid[(size_t)q * nslots + i] = i == 0 ? 1 : 0;
+  for (int i = threadIdx.x; i < nslots * a.mw; i += SEL_THREADS)
+    a.masks[(size_t)q * nslots * a.mw + i] = 0;
   __shared__ float scratch[SEL_THREADS / 64];
   const int d4 = a.d / 4;
   for (int t = 0; t < win; ++t) {
@@ -516,7 +692,13 @@ static void launch_select_t(const SelectArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  if (a.rmax > 1) {  // some sequence holds r > 1 token states
+  if (a.beam > 1) {
+    const dim3 grid(a.n_seqs * (a.B + 1));
+    if (a.act == ACT_F32)
+      hipLaunchKernelGGL(select_beam_kernel<float>, grid, dim3(SELB_THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL(select_beam_kernel<bf16>, grid, dim3(SELB_THREADS), 0, s, a);
+  } else if (a.rmax > 1) {  // some sequence holds r > 1 token states
     const dim3 grid(a.n_seqs * (a.B + 1));
     if (a.act == ACT_F32)
       hipLaunchKernelGGL(select_win_kernel<float>, grid, dim3(SELW_THREADS), 0, s, a);

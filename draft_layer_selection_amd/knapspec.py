@@ -28,6 +28,7 @@ KNAPSPEC_RETURN_DECISIONS = 1
 KNAPSPEC_RETURN_MARGINS = 2
 KNAPSPEC_ALPHA_LM_HEAD = 4
 KNAPSPEC_WINDOW_MAX = 8
+KNAPSPEC_BEAM_MAX = 8
 KERNEL_CLASSES = ["init", "gemm_qkv", "qkv_rope", "attention", "combine", "gemm_o",
                   "gemm_gate_up", "gemm_down", "select", "lm_head"]
 
@@ -37,7 +38,7 @@ class knapspec_model_desc(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ff", C.c_int32),
                 ("dtype", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
                 ("max_budgets", C.c_int32), ("max_seqs", C.c_int32), ("max_ctx", C.c_int32),
-                ("max_window", C.c_int32)]
+                ("max_window", C.c_int32), ("max_beam", C.c_int32)]
 
 
 class knapspec_layer_weights(C.Structure):
@@ -60,7 +61,7 @@ class knapspec_solve_args(C.Structure):
     _fields_ = [("n_seqs", C.c_int32), ("seqs", C.POINTER(knapspec_seq)),
                 ("n_budgets", C.c_int32), ("gamma_min", C.c_int32), ("gamma_max", C.c_int32),
                 ("tau", C.c_float), ("max_skip_weight", C.c_int32), ("flags", C.c_int32),
-                ("hip_stream", C.c_void_p)]
+                ("hip_stream", C.c_void_p), ("beam", C.c_int32)]
 
 
 class knapspec_result(C.Structure):
@@ -264,7 +265,7 @@ class Model:
 
     def solve(self, seqs: List[dict], n_budgets: int, gamma, tau: float = -math.inf,
               max_skip_weight: int = -1, flags: int = 0, stream=None,
-              result: Optional[Result] = None) -> Result:
+              result: Optional[Result] = None, beam: int = 1) -> Result:
         """seqs: dicts with ctx (int), k_cache / v_cache (lists of device tensors per layer,
         [hkv][capacity][dh]), x0 (device float32 [window][d] or [d]) and optionally window
         (int, default 1)."""
@@ -273,7 +274,8 @@ class Model:
         carr, keep = self._seq_array(seqs)
         s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
         args = knapspec_solve_args(S, carr, int(n_budgets), int(gamma[0]), int(gamma[1]),
-                                   float(tau), int(max_skip_weight), int(flags), C.c_void_p(s))
+                                   float(tau), int(max_skip_weight), int(flags), C.c_void_p(s),
+                                   int(beam))
         res = result if result is not None else Result(
             S, n_budgets, 2 * self.n_layers, self.mw, flags,
             windows=[int(sq.get("window", 1)) for sq in seqs])

@@ -56,6 +56,7 @@ extern "C" {
 #define KNAPSPEC_ALPHA_LM_HEAD 4    /* TPT acceptance from the LM head (knapspec_set_lm_head) */
 
 #define KNAPSPEC_WINDOW_MAX 8 /* largest r of an r-token window */
+#define KNAPSPEC_BEAM_MAX 8   /* largest beam width of the beam variant of the DP */
 
 typedef struct knapspec_model knapspec_model; /* opaque */
 
@@ -75,6 +76,8 @@ typedef struct {
   int32_t max_ctx;     /* largest ctx_len a solve may use */
   int32_t max_window;  /* largest r a sequence may use (0 or 1: single-token states;
                           <= KNAPSPEC_WINDOW_MAX); the workspace scales with it */
+  int32_t max_beam;    /* largest beam a solve may use (0 or 1: the one-state DP only;
+                          <= KNAPSPEC_BEAM_MAX); the workspace scales with it */
 } knapspec_model_desc;
 
 /* Device pointers of one layer's weights, row-major [out][in], in desc.dtype:
@@ -131,8 +134,18 @@ typedef struct {
   int32_t gamma_min, gamma_max; /* TPT grid, 1 <= gamma_min <= gamma_max <= 64 */
   float tau;                  /* prune a cell whose kept cosine < tau; -INFINITY disables */
   int32_t max_skip_weight;    /* prune cells whose skipped weight P_i - b exceeds it; <0 off */
-  int32_t flags;              /* KNAPSPEC_RETURN_DECISIONS | KNAPSPEC_RETURN_MARGINS */
+  int32_t flags;              /* KNAPSPEC_RETURN_DECISIONS | KNAPSPEC_RETURN_MARGINS |
+                                 KNAPSPEC_ALPHA_LM_HEAD */
   void* hip_stream;           /* stream the work is enqueued on (NULL = default stream) */
+  int32_t beam;               /* states kept per (item, budget) cell: 0 or 1 = the one-state
+                                 DP; k in 2..desc.max_beam = the beam variant (review,
+                                 "Reading between the lines": an exact or beam-search variant
+                                 measures the greedy rule's headroom).  Each cell keeps the k
+                                 candidates -- its k skip states and the item applied to the k
+                                 states of b - w_i -- with the highest cosine (ties: skip slots,
+                                 then execute slots, each in slot order); results report each
+                                 budget's best set.  Decisions and margins are those of the
+                                 one-state DP: with beam > 1 their flags are EINVAL. */
 } knapspec_solve_args;
 
 /* Caller-allocated HOST arrays; "W" = knapspec_mask_words(n_layers), L2 = 2 * n_layers. */

@@ -27,7 +27,8 @@ class DeviceProblem:
 
     def __init__(self, wl: Workload, seed: int = 0, ctxs: Optional[List[int]] = None,
                  caps: Optional[List[int]] = None, keep_host: bool = False,
-                 max_budgets: Optional[int] = None, window: int = 1, lm_vocab: int = 0):
+                 max_budgets: Optional[int] = None, window: int = 1, lm_vocab: int = 0,
+                 max_beam: int = 1):
         import torch
 
         from draft_layer_selection_amd import knapspec as ks
@@ -73,7 +74,7 @@ class DeviceProblem:
                     dtype=ks.KNAPSPEC_BF16 if s.dtype == "bf16" else ks.KNAPSPEC_F32,
                     rms_eps=s.rms_eps, rope_theta=s.rope_theta,
                     max_budgets=max_budgets or wl.n_budgets, max_seqs=len(self.ctxs),
-                    max_ctx=max(self.caps), max_window=self.window)
+                    max_ctx=max(self.caps), max_window=self.window, max_beam=max_beam)
         torch.cuda.synchronize()
         self.model = ks.Model(desc, self.layers)
         lat = wl.latency
@@ -107,10 +108,11 @@ class DeviceProblem:
         return [c + r * self.wl.tokens_per_resolve for c in self.ctxs]
 
     def solve(self, n_budgets=None, gamma=None, tau=-math.inf, max_skip_weight=-1, flags=0,
-              ctxs=None, result=None, resolve=None):
+              ctxs=None, result=None, resolve=None, beam=1):
         wl = self.wl
         return self.model.solve(self.seq_args(ctxs, resolve), n_budgets or wl.n_budgets,
-                                gamma or wl.gamma, tau, max_skip_weight, flags, result=result)
+                                gamma or wl.gamma, tau, max_skip_weight, flags, result=result,
+                                beam=beam)
 
     def close(self):
         self.model.close()
