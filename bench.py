@@ -28,22 +28,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def item_rows(w, B):
-    """Rows of each item's GEMM per sequence: reachable sources s with s + w_i <= B-1, plus the
-    reference row (same bookkeeping the library does; measurement only)."""
-    reach = [False] * B
-    reach[0] = True
+def item_rows(w, B, beam=1):
+    """Rows of each item's GEMM per sequence: the source states (budgets s with s + w_i <= B-1,
+    up to ``beam`` states each -- the number of distinct subsets of weight s, capped), plus the
+    reference row, and the live states after the item (same bookkeeping as the library;
+    measurement only)."""
+    cnt = [0] * B
+    cnt[0] = 1
     rows, live = [], []
     for wi in w:
-        src = [s for s in range(B) if reach[s] and s + wi <= B - 1]
-        rows.append(len(src) + 1)
-        for s in src:
-            reach[s + wi] = True
-        live.append(sum(reach))
+        src = sum(cnt[s] for s in range(B) if s + wi <= B - 1)
+        rows.append(src + 1)
+        cnt = [min(beam, cnt[b] + (cnt[b - wi] if b >= wi else 0)) for b in range(B)]
+        live.append(sum(cnt))
     return rows, live
 
 
-def algorithmic_work(wl, w_per_seq, ctxs, window=1, vocab=0):
+def algorithmic_work(wl, w_per_seq, ctxs, window=1, vocab=0, beam=1):
     """Minimum HBM bytes and FLOPs of one solve, per kernel class and in total.
 
     Per item: its weight matrix once; for Attention items the sequence's K and V cache once;
@@ -61,7 +62,7 @@ def algorithmic_work(wl, w_per_seq, ctxs, window=1, vocab=0):
     L2 = 2 * s.n_layers
     per_item_rows = []
     for q, w in enumerate(w_per_seq):
-        rows, live = item_rows(list(w), wl.n_budgets)
+        rows, live = item_rows(list(w), wl.n_budgets, beam)
         per_item_rows.append(([x * window for x in rows], [x * window for x in live]))
     for i in range(L2):
         R = sum(pr[0][i] for pr in per_item_rows)
@@ -282,6 +283,8 @@ def main():
     ap.add_argument("--commands", default="")
     ap.add_argument("--window", type=int, default=1,
                     help="tokens per DP state (r-token window); 1 = the single-token solve")
+    ap.add_argument("--beam", type=int, default=1,
+                    help="states kept per DP cell (the beam variant); 1 = the one-state DP")
     ap.add_argument("--lm-vocab", type=int, default=0,
                     help="also run the LM-head acceptance estimate with this many rows")
     args = ap.parse_args()
@@ -307,10 +310,10 @@ def main():
     want_cpu = not args.no_cpu_baseline
     t0 = time.time()
     log(f"[bench] generating and uploading {wl.name} inputs ...")
-    if args.window != 1 or args.lm_vocab:
+    if args.window != 1 or args.lm_vocab or args.beam != 1:
         want_cpu = False  # the CPU baseline leg covers the single-token solve only
     prob = DeviceProblem(wl, args.seed, keep_host=want_cpu, window=args.window,
-                         lm_vocab=args.lm_vocab)
+                         lm_vocab=args.lm_vocab, max_beam=args.beam)
     flags = prob.ks.KNAPSPEC_ALPHA_LM_HEAD if args.lm_vocab else 0
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; warmup {args.warmup}")
     # one step = one solve; for a multi-sequence preset one step is its whole re-solve
@@ -320,9 +323,9 @@ def main():
 
     def step(res):
         if not multi:
-            return prob.solve(result=res, flags=flags)
+            return prob.solve(result=res, flags=flags, beam=args.beam)
         for r in range(prob.n_resolves):
-            res = prob.solve(resolve=r, flags=flags)
+            res = prob.solve(resolve=r, flags=flags, beam=args.beam)
         return res
 
     res = None
@@ -359,7 +362,7 @@ def main():
     for r in range(prob.n_resolves):
         ctxs = prob.resolve_ctxs(r) if multi else prob.ctxs
         w_per_seq = [ko_weights(wl, c) for c in ctxs]
-        c_r, t_r = algorithmic_work(wl, w_per_seq, ctxs, args.window, args.lm_vocab)
+        c_r, t_r = algorithmic_work(wl, w_per_seq, ctxs, args.window, args.lm_vocab, args.beam)
         if cls is None:
             cls, tot = c_r, t_r
         else:
@@ -429,7 +432,7 @@ def main():
                    "heads_q_kv": [wl.shape.n_q_heads, wl.shape.n_kv_heads],
                    "head_dim": wl.shape.head_dim, "d_ff": wl.shape.d_ff, "ctx": prob.ctxs,
                    "budgets": wl.n_budgets, "gamma": list(wl.gamma), "n_seqs": len(prob.ctxs),
-                   "window": args.window, "lm_vocab": args.lm_vocab,
+                   "window": args.window, "lm_vocab": args.lm_vocab, "beam": args.beam,
                    "parallelism": "single-gpu"},
         "achieved_hbm_gbs": round(achieved_gbs, 1),
         "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),

@@ -13,6 +13,10 @@ Experiments the KnapSpec pages describe around the DP, run on seeded synthetic i
   an MLP item, timed on the device (knapspec_profile_items), with t_attn(n) = a + b*n fitted
   by least squares (knapspec_fit_latency) -- the measured latency model the weights can use
   instead of the bandwidth stand-in of the presets.
+* Beam gap ("KnapSpec" review, "Reading between the lines": an exact or beam-search variant
+  shows the greedy rule's headroom): the same problem solved with the one-state DP and with
+  beams of k states per cell; per budget, how much higher the best set's cosine is, and how
+  the TPT pick and its value change.
 
 Everything runs through the library (no arithmetic of the method here); this module only
 arranges calls and tabulates what the library returns.  Command line:
@@ -104,6 +108,43 @@ def tau_ablation(prob, taus: Sequence[float], reps: int = 5, n_budgets: Optional
     return rows
 
 
+def beam_gap(prob, beams: Sequence[int], reps: int = 3, band: Optional[float] = None) -> List[dict]:
+    """Per beam width: solve time (median host time of reps) and, against beam 1, how many
+    valid budgets end with a set whose cosine is higher by more than ``band`` (default: the
+    parity band of the dtype, 2e-3 bf16 / 1e-5 float32 -- smaller differences are rounding
+    of differently batched rows), the largest and mean cosine gain, and the TPT pick."""
+    if band is None:
+        band = 2e-3 if prob.wl.shape.dtype == "bf16" else 1e-5
+    import torch
+
+    rows = []
+    base = None
+    for k in beams:
+        res = prob.solve(beam=int(k))
+        for _ in range(2):  # untimed: the first solves of a configuration capture its graph
+            prob.solve(beam=int(k))
+        times = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            prob.solve(beam=int(k))
+            times.append(time.perf_counter() - t0)
+        valid = res.valid[0].astype(bool)
+        cos = res.cos[0].astype(np.float64)
+        row = {"beam": int(k), "solve_ms": 1e3 * float(np.median(times)),
+               "valid_budgets": int(valid.sum()), "pick_budget": int(res.best_budget[0]),
+               "pick_gamma": int(res.best_gamma[0]), "best_tpt": float(res.best_tpt[0])}
+        if base is None:
+            base = cos
+        else:
+            gain = np.where(valid, cos - base, 0.0)
+            row.update(band=band, better_budgets=int(np.sum(gain > band)),
+                       max_cos_gain=float(gain.max()), mean_cos_gain=float(gain[valid].mean()),
+                       p90_cos_gain=float(np.percentile(gain[valid], 90)))
+        rows.append(row)
+    return rows
+
+
 def latency_profile(prob, ctx_list: Sequence[int], reps: int = 8) -> dict:
     """Measured item latencies and the fitted linear attention model (microseconds)."""
     seq = prob.seq_args([max(ctx_list)])[0]
@@ -121,6 +162,7 @@ def main(argv=None):
     ap.add_argument("--ctx", default="1024,2048,4096,8192,16384,32768")
     ap.add_argument("--taus", default="-inf,0.0,0.3,0.5,0.7,0.9")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--beams", default="", help="beam widths for the beam-gap table, e.g. 1,2,4,8")
     ap.add_argument("--profiled", action="store_true",
                     help="also solve the sweep with the measured (fitted) latency model")
     ap.add_argument("--seed", type=int, default=0)
@@ -135,13 +177,24 @@ def main(argv=None):
     ctx_list = [int(x) for x in args.ctx.split(",")]
     taus = [float(x) for x in args.taus.split(",")]
     cap = max(max(ctx_list), wl.ctx)
-    prob = DeviceProblem(wl, args.seed, ctxs=[wl.ctx], caps=[cap])
+    beams = [int(x) for x in args.beams.split(",")] if args.beams else []
+    prob = DeviceProblem(wl, args.seed, ctxs=[wl.ctx], caps=[cap],
+                         max_beam=max(beams) if beams else 1)
     out = {"workload": wl.name, "layers": wl.shape.n_layers, "n_budgets": wl.n_budgets,
            "latency_model": "bandwidth-bound stand-in (8 TB/s)",
            "sweep": context_sweep(prob, ctx_list)}
     print(json.dumps({"sweep": out["sweep"]}), flush=True)
     out["tau_ablation"] = tau_ablation(prob, taus, reps=args.reps)
     print(json.dumps({"tau_ablation": out["tau_ablation"]}), flush=True)
+    if beams:
+        out["beam_gap"] = beam_gap(prob, beams, reps=args.reps)
+        print(json.dumps({"beam_gap": out["beam_gap"]}), flush=True)
+    if len(set(ctx_list)) < 2:  # a line fit needs two context lengths
+        prob.close()
+        if args.out:
+            with open(args.out, "w") as f:
+                json.dump(out, f, indent=1)
+        return
     prof = latency_profile(prob, ctx_list, reps=max(args.reps, 8))
     out["latency_profile"] = prof
     print(json.dumps({"latency_profile": prof}), flush=True)
