@@ -35,6 +35,9 @@ Pins (tests that tie this code to something other than itself):
   * knapsack_dp_beam            beam 1 is knapsack_dp exactly; a beam at least as wide as the
                                 number of subsets of any weight is exhaustive enumeration
                                 (the best subset per budget, brute force on small decoders).
+  * draft_verify                with every item executed the draft is the target model, so the
+                                verification accepts every draft token; the verification block
+                                equals token-by-token decoding (window pin above).
 Parity unpinned: the full DP at the Qwen3-1.7B, Llama-3-8B and Llama-3-70B shapes has no
 independent check beyond the pins above and the per-mask self-consistency of the results.
 """
@@ -605,6 +608,91 @@ def alpha_lm_head(states: np.ndarray, valid: np.ndarray, ref: np.ndarray, w_lm: 
     tref, _ = greedy_tokens(ref, w_lm, eps)
     a = (tok == tref[None, :]).sum(axis=1).astype(F64) / r
     return np.where(np.asarray(valid, dtype=bool), a, 0.0)
+
+
+@dataclasses.dataclass
+class DraftVerify:
+    draft: np.ndarray          # int64 [gamma] greedy tokens of the masked draft
+    draft_margin: np.ndarray   # float64 [gamma] their top-2 logit gaps
+    verify: np.ndarray         # int64 [gamma + 1] the target's greedy tokens on the block
+    verify_margin: np.ndarray  # float64 [gamma + 1]
+    accepted: int              # leading draft tokens equal to the target's
+
+
+def draft_verify(shape: DecoderShape, layers, kv, x0: np.ndarray, ctx: int, bits: np.ndarray,
+                 gamma: int, w_lm: np.ndarray) -> DraftVerify:
+    """One self-speculative step with the chosen layer set: gamma draft tokens, then one
+    verification pass of gamma + 1 tokens (review, "The reading" and "What carries the
+    argument": the draft runs the selected items, the target verifies).
+
+    Readings (the pages print no decode loop): tokens are greedy (argmax of the LM head over
+    the RMSNorm'd final state, ties to the lower index); a token's input state is its LM-head
+    row (tied embeddings); draft token t sits at position ctx + t and its executed Attention
+    items append their key/value there, so later draft tokens attend to the cache 0..ctx-1 and
+    to the earlier draft tokens' entries of the layers the draft ran; the verification runs
+    every item on [x0, e(y_0), .., e(y_{gamma-1})] at positions ctx .. ctx+gamma as one causal
+    block over the cache 0..ctx-1; accepted = the number of leading t with y_t equal to the
+    target's token z_t.  kv is not modified.
+    """
+    s = shape
+    hq, hkv, dh = s.n_q_heads, s.n_kv_heads, s.head_dim
+    n_items = 2 * s.n_layers
+    W = widen(w_lm)
+    cap = ctx + gamma + 1
+    caches = []
+    for l in range(s.n_layers):
+        kc, vc = kv[l]
+        k2 = np.zeros((hkv, cap, dh), F32)
+        v2 = np.zeros((hkv, cap, dh), F32)
+        k2[:, :ctx] = widen(kc[:, :ctx])
+        v2[:, :ctx] = widen(vc[:, :ctx])
+        caches.append((k2, v2))
+    wts = [{k: widen(v) for k, v in layers[l].items()} for l in range(s.n_layers)]
+
+    def own_kv(x, w, pos):
+        xn = rmsnorm(x[None], s.rms_eps)
+        qkv = (xn @ w["w_qkv"].T)[0]
+        k = qkv[hq * dh:(hq + hkv) * dh].reshape(hkv, dh)
+        v = qkv[(hq + hkv) * dh:].reshape(hkv, dh)
+        c, sn = rope_cos_sin(pos, dh, s.rope_theta)
+        return rope(k, c, sn), v
+
+    x = np.asarray(x0, F32).copy()
+    inputs = [x.copy()]
+    draft, dmar = [], []
+    for t in range(gamma):
+        pos = ctx + t
+        for i in range(n_items):
+            if not bits[i]:
+                continue
+            l, w = i // 2, wts[i // 2]
+            if i % 2 == 0:
+                kc, vc = caches[l]
+                k, v = own_kv(x, w, pos)
+                x = attention_item(x[None], w["w_qkv"], w["w_o"], kc, vc, pos, s)[0]
+                kc[:, pos], vc[:, pos] = k, v
+            else:
+                x = mlp_item(x[None], w["w_gate_up"], w["w_down"], s)[0]
+        tok, mar = greedy_tokens(x[None], W, s.rms_eps)
+        draft.append(int(tok[0]))
+        dmar.append(float(mar[0]))
+        x = W[int(tok[0])].astype(F32).copy()
+        inputs.append(x.copy())
+    X = np.stack(inputs)[None]                      # [1][gamma+1][d]
+    for i in range(n_items):
+        l, w = i // 2, wts[i // 2]
+        if i % 2 == 0:
+            X = attention_item_window(X, w["w_qkv"], w["w_o"], kv[l][0], kv[l][1], ctx, s)
+        else:
+            M, r, d = X.shape
+            X = mlp_item(X.reshape(M * r, d), w["w_gate_up"], w["w_down"], s).reshape(M, r, d)
+    ver, vmar = greedy_tokens(X[0], W, s.rms_eps)
+    acc = 0
+    while acc < gamma and draft[acc] == int(ver[acc]):
+        acc += 1
+    return DraftVerify(draft=np.array(draft, dtype=np.int64), draft_margin=np.array(dmar),
+                       verify=np.asarray(ver, dtype=np.int64), verify_margin=np.asarray(vmar),
+                       accepted=acc)
 
 
 # --------------------------------------------------------------------------------------
