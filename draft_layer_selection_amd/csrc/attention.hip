@@ -545,6 +545,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   for (int e = 0; e < EPL; ++e) out[e] = from_f32<T>(num[e] * inv);
 }
 
+template <class T>
+__global__ __launch_bounds__(256) void kv_append_kernel(const float* kself, const float* vself,
+                                                       int n, int hkv, int dh, T* kc, T* vc,
+                                                       int cap, int pos0) {
+  const size_t total = (size_t)n * hkv * dh;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int e = (int)(i % dh);
+  const int c = (int)((i / dh) % hkv);
+  const int t = (int)(i / ((size_t)dh * hkv));
+  const size_t dst = ((size_t)c * cap + pos0 + t) * dh + e;
+  kc[dst] = from_f32<T>(kself[i]);
+  vc[dst] = from_f32<T>(vself[i]);
+}
+
 }  // namespace
 
 int attention_qblock(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? QB : 64; }
@@ -558,6 +573,20 @@ hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s) {
     hipLaunchKernelGGL(qkv_kernel<float>, grid, block, 0, s, a);
   else
     hipLaunchKernelGGL(qkv_kernel<bf16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const float* kself, const float* vself, int n, int hkv, int dh,
+                            void* kc, void* vc, int cap, int pos0, int act, hipStream_t s) {
+  const size_t total = (size_t)n * hkv * dh;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (act == ACT_F32)
+    hipLaunchKernelGGL(kv_append_kernel<float>, grid, block, 0, s, kself, vself, n, hkv, dh,
+                       (float*)kc, (float*)vc, cap, pos0);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<bf16>, grid, block, 0, s, kself, vself, n, hkv, dh,
+                       (bf16*)kc, (bf16*)vc, cap, pos0);
   return hipGetLastError();
 }
 

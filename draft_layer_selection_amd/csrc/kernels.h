@@ -17,7 +17,7 @@ enum ActType : int { ACT_F32 = 0, ACT_BF16 = 1 };
 // ---------------------------------------------------------------------------------------
 enum GemmMode : int { GEMM_PARTIAL = 0, GEMM_SWIGLU = 1 };
 
-constexpr int WIN_MAX = 8;   // largest window r (tokens per DP state)
+constexpr int WIN_MAX = 16;  // largest window r (tokens per DP state or verification block)
 constexpr int BEAM_MAX = 8;  // largest beam width (states kept per DP cell)
 
 struct GemmArgs {
@@ -190,6 +190,18 @@ struct LmArgmaxArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 hipError_t launch_lm_argmax(const LmArgmaxArgs& a, hipStream_t s);
+
+// Decode-loop helpers (masked draft step and verification):
+// carry: for rows t < n, state[t] = src[t] and xa[t] = RMSNorm(src[t]) in the activation type.
+hipError_t launch_carry(const float* src, int n, int d, float eps, float* state, void* xa,
+                        int act, hipStream_t s);
+// embed: out[t] = LM-head row idx[t] (tied embedding), widened to float32, for t < n.
+hipError_t launch_embed(const void* w_lm, const int* idx, int n, int d, int act, float* out,
+                        hipStream_t s);
+// kv_append: the own keys/values of rows t < n (kself/vself [n][hkv][dh]) into a cache
+// [hkv][cap][dh] of the activation type at positions pos0 + t.
+hipError_t launch_kv_append(const float* kself, const float* vself, int n, int hkv, int dh,
+                            void* kc, void* vc, int cap, int pos0, int act, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);

@@ -1550,3 +1550,332 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
   *mlp_us = median_of(samples);
   return KNAPSPEC_OK;
 }
+
+// ------------------------------------------------------------------------------------------
+// Masked draft step and verification pass: gamma greedy draft tokens through the chosen items
+// (M = 1 rows, key/value appends at positions ctx .. ctx+gamma-1), then every item on the
+// gamma + 1 tokens as one causal block (the window path), all on one stream
+// ------------------------------------------------------------------------------------------
+namespace {
+
+int run_gemm(knapspec_model* m, hipStream_t st, const void* A, int lda, int R, const void* W,
+             int K, int N, int mode, int* splits) {
+  ks::GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.R = R;
+  g.W = W;
+  g.K = K;
+  g.N = N;
+  g.mode = mode;
+  const ks::GemmPlan p = ks::plan_gemm(m->act, R, N, K, mode, m->desc.d_ff, m->p_floats);
+  g.ng = p.ng;
+  g.mb = p.mb;
+  g.m_tiles = p.m_tiles;
+  g.n_tiles = p.n_tiles;
+  g.splits = p.splits;
+  g.k_chunk = p.k_chunk;
+  if (mode == ks::GEMM_SWIGLU) {
+    g.H = m->h;
+    g.ldh = m->desc.d_ff;
+    g.ff = m->desc.d_ff;
+  } else {
+    g.P = m->P;
+    g.ldp = N;
+  }
+  *splits = g.splits;
+  HIPCHK(ks::launch_gemm(g, m->act, st));
+  return KNAPSPEC_OK;
+}
+
+// greedy token of rows 0..R-1 of the activations (already RMSNorm'd) into m->lm_idx
+int run_lm_greedy(knapspec_model* m, hipStream_t st, int R) {
+  const int D = m->desc.d_model;
+  const size_t per_chunk = m->p_floats / (size_t)std::max(1, R);
+  const int vc = (int)std::min<size_t>((size_t)m->lm_vocab,
+                                       std::max<size_t>(64, per_chunk / 256 * 256));
+  for (int v0 = 0; v0 < m->lm_vocab; v0 += vc) {
+    const int nc = std::min(vc, m->lm_vocab - v0);
+    int sp = 1;
+    int rc = run_gemm(m, st, m->xa, D, R, (const char*)m->lm_w + (size_t)v0 * D * m->elem, D, nc,
+                      ks::GEMM_PARTIAL, &sp);
+    if (rc) return rc;
+    ks::LmArgmaxArgs la{};
+    la.P = m->P;
+    la.splits = sp;
+    la.R = R;
+    la.ldp = nc;
+    la.ncols = nc;
+    la.col0 = v0;
+    la.first = v0 == 0;
+    la.best_val = m->lm_val;
+    la.best_idx = m->lm_idx;
+    HIPCHK(ks::launch_lm_argmax(la, st));
+  }
+  return KNAPSPEC_OK;
+}
+
+}  // namespace
+
+KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
+                                 const uint64_t* mask, int32_t gamma, void* hip_stream,
+                                 int32_t* draft_tokens, int32_t* verify_tokens,
+                                 int32_t* accepted, double* draft_us, double* verify_us) {
+  if (!m || !seq || !mask || !draft_tokens || !verify_tokens || !accepted || !draft_us ||
+      !verify_us)
+    return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  const knapspec_model_desc& d = m->desc;
+  if (!m->lm_w) return fail(KNAPSPEC_EINVAL, "no LM head (knapspec_set_lm_head)");
+  if (gamma < 1 || gamma + 1 > KNAPSPEC_WINDOW_MAX)
+    return fail(KNAPSPEC_EINVAL, "gamma must be in [1, %d]", KNAPSPEC_WINDOW_MAX - 1);
+  const int ctx = seq->ctx_len;
+  if (ctx < 0 || ctx > d.max_ctx) return fail(KNAPSPEC_EINVAL, "ctx_len must be in [0, %d]", d.max_ctx);
+  if (seq->ctx_capacity < ctx + gamma + 1)
+    return fail(KNAPSPEC_EINVAL, "ctx_capacity must hold ctx_len + gamma + 1 positions");
+  if (!seq->x0) return fail(KNAPSPEC_EINVAL, "x0 is NULL");
+  if (seq->window > 1) return fail(KNAPSPEC_EINVAL, "x0 must be the current token (window <= 1)");
+  if (!seq->k_cache || !seq->v_cache) return fail(KNAPSPEC_EINVAL, "cache arrays NULL");
+  for (int l = 0; l < d.n_layers; ++l)
+    if (!seq->k_cache[l] || !seq->v_cache[l])
+      return fail(KNAPSPEC_EINVAL, "layer %d: NULL cache pointer", l);
+  const int n = gamma + 1;
+  if (m->Rmax < n) return fail(KNAPSPEC_EINVAL, "workspace rows < gamma + 1");
+  int cur_dev = -1;
+  if (hipGetDevice(&cur_dev) != hipSuccess || cur_dev != m->device)
+    return fail(KNAPSPEC_EINVAL, "current HIP device differs from the model's device");
+
+  const int hq = d.n_q_heads, hkv = d.n_kv_heads, dh = d.head_dim, D = d.d_model;
+  const int G = hq / hkv;
+  const int L2 = m->L2;
+  const int qb_rows = ks::attention_qblock(m->act, dh);
+  const int qb_max = (G * n + qb_rows - 1) / qb_rows;
+  const size_t max_work = (size_t)hkv * qb_max * ASPLIT_MAX;
+  // tables: rope [n][dh] | row_seq, row_state, row_tok [n] | AttnSeq [n][layers] (draft
+  // steps, then the verification; each with the layer's cache) | work lists [n][max_work] |
+  // x_in [n][d] (the verification block's input rows) | tok [gamma] | host-side results
+  Carver c;
+  const int nl = d.n_layers;
+  const size_t o_rope = c.take((size_t)n * dh * 4);
+  const size_t o_rowseq = c.take((size_t)n * 4);
+  const size_t o_rowstate = c.take((size_t)n * 4);
+  const size_t o_rowtok = c.take((size_t)n * 4);
+  const size_t o_aseq = c.take((size_t)n * nl * sizeof(ks::AttnSeq));
+  const size_t o_work = c.take((size_t)n * max_work * sizeof(int4));
+  const size_t o_xin = c.take((size_t)n * D * 4);
+  const size_t o_tok = c.take((size_t)gamma * 4);
+  const size_t o_hres = c.take((size_t)(gamma + n) * 4);
+  const size_t upload_bytes = o_xin;  // everything before the device-only rows
+  const size_t bytes = c.off;
+  if (m->pr_bytes < bytes) {
+    if (m->pr_dev) (void)hipFree(m->pr_dev);
+    if (m->pr_host) (void)hipHostFree(m->pr_host);
+    m->pr_dev = m->pr_host = nullptr;
+    m->pr_bytes = 0;
+    if (hipMalloc((void**)&m->pr_dev, bytes) != hipSuccess ||
+        hipHostMalloc((void**)&m->pr_host, bytes, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(KNAPSPEC_ENOMEM, "draft/verify table allocation failed");
+    }
+    m->pr_bytes = bytes;
+  }
+  char* hp = m->pr_host;
+  char* dp = m->pr_dev;
+  float* rope = (float*)(hp + o_rope);
+  for (int t = 0; t < n; ++t) {
+    const double pos = (double)ctx + t;
+    for (int j = 0; j < dh / 2; ++j) {
+      const double ang = pos * std::pow((double)d.rope_theta, -2.0 * j / (double)dh);
+      rope[(size_t)t * dh + j] = (float)std::cos(ang);
+      rope[(size_t)t * dh + dh / 2 + j] = (float)std::sin(ang);
+    }
+    ((int32_t*)(hp + o_rowseq))[t] = 0;
+    ((int32_t*)(hp + o_rowstate))[t] = t;  // state rows 0..gamma serve as the running states
+    ((int32_t*)(hp + o_rowtok))[t] = t;
+  }
+  // attention plans: draft step t reads ctx + t cached positions with one row; the
+  // verification reads ctx positions with n rows (window tokens 0..gamma)
+  const int slots = m->n_cus * ks::attention_wgs_per_cu(m->act, dh);
+  std::vector<int> nwork(n);
+  for (int k = 0; k < n; ++k) {
+    const bool ver = k == gamma;
+    const int actx = ver ? ctx : ctx + k;
+    const int M = ver ? n : 1;
+    const int qbs = (G * M + qb_rows - 1) / qb_rows;
+    std::vector<int> pairs{hkv * qbs}, tiles{(actx + 63) / 64}, nsplit;
+    std::vector<size_t> prow{(size_t)M * hq};
+    plan_attention_splits(pairs, tiles, prow, slots, ASPLIT_MAX, m->part_slots, nsplit);
+    const int ns = nsplit[0];
+    const int chunk = ns > 0 ? (tiles[0] + ns - 1) / ns * 64 : 64;
+    ks::AttnSeq as{};
+    as.k = nullptr;  // set per layer below
+    as.v = nullptr;
+    as.ctx = actx;
+    as.cap = seq->ctx_capacity;
+    as.row_off = 0;
+    as.M = M;
+    as.nsplit = actx > 0 ? (actx + chunk - 1) / chunk : 0;
+    as.chunk = chunk;
+    as.part_off = 0;
+    as.pad0 = M;
+    for (int l = 0; l < nl; ++l) {
+      as.k = seq->k_cache[l];
+      as.v = seq->v_cache[l];
+      ((ks::AttnSeq*)(hp + o_aseq))[(size_t)k * nl + l] = as;
+    }
+    int4* work = (int4*)(hp + o_work) + (size_t)k * max_work;
+    int nw = 0;
+    for (int cc = 0; cc < hkv; ++cc)
+      for (int sp = 0; sp < as.nsplit; ++sp)
+        for (int qb = 0; qb < qbs; ++qb) work[nw++] = make_int4(0, cc, qb, sp);
+    nwork[k] = nw;
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  for (auto& e : ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      for (auto& f : ev)
+        if (f) (void)hipEventDestroy(f);
+      return fail(KNAPSPEC_EHIP, "event creation failed");
+    }
+  struct EvGuard {
+    hipEvent_t* e;
+    ~EvGuard() {
+      for (int i = 0; i < 3; ++i)
+        if (e[i]) (void)hipEventDestroy(e[i]);
+    }
+  } guard{ev};
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  const int32_t* d_rowseq = (const int32_t*)(dp + o_rowseq);
+  const int32_t* d_rowstate = (const int32_t*)(dp + o_rowstate);
+  const int32_t* d_rowtok = (const int32_t*)(dp + o_rowtok);
+  float* x_in = (float*)(dp + o_xin);
+  int32_t* d_tok = (int32_t*)(dp + o_tok);
+
+  // one item on R rows (R = 1 in the draft, n in the verification); the attention table
+  // entry k carries the cached-position count and the row count
+  auto item = [&](int i, int R, int k, int pos0) -> int {
+    const int l = i / 2;
+    const knapspec_layer_weights& W = m->layers[l];
+    int splits = 1, rc;
+    if (i % 2 == 0) {
+      rc = run_gemm(m, st, m->xa, D, R, W.w_qkv, D, m->nqkv, ks::GEMM_PARTIAL, &splits);
+      if (rc) return rc;
+      ks::QkvArgs qa{};
+      qa.P = m->P;
+      qa.splits = splits;
+      qa.R = R;
+      qa.ldp = m->nqkv;
+      qa.hq = hq;
+      qa.hkv = hkv;
+      qa.dh = dh;
+      qa.rope = (const float*)(dp + o_rope) + (size_t)(R == 1 ? k : 0) * dh;
+      qa.row_seq = d_rowseq;
+      qa.row_tok = d_rowtok;
+      qa.wmax = R == 1 ? 1 : n;
+      qa.Q = m->q;
+      qa.kself = m->kself;
+      qa.vself = m->vself;
+      HIPCHK(ks::launch_qkv(qa, m->act, st));
+      HIPCHK(ks::launch_kv_append(m->kself, m->vself, R, hkv, dh,
+                                  const_cast<void*>(seq->k_cache[l]),
+                                  const_cast<void*>(seq->v_cache[l]), seq->ctx_capacity, pos0,
+                                  m->act, st));
+      ks::AttnArgs aa{};
+      aa.Q = m->q;
+      aa.hq = hq;
+      aa.hkv = hkv;
+      aa.dh = dh;
+      aa.work = (const int4*)(dp + o_work) + (size_t)k * max_work;
+      aa.seqs = (const ks::AttnSeq*)(dp + o_aseq) + (size_t)k * nl + l;
+      aa.Opart = m->Opart;
+      aa.Mpart = m->Mpart;
+      aa.Lpart = m->Lpart;
+      aa.scale_log2 = scale_log2;
+      HIPCHK(ks::launch_attention(aa, m->act, nwork[k], st));
+      ks::CombineArgs ca{};
+      ca.Q = m->q;
+      ca.kself = m->kself;
+      ca.vself = m->vself;
+      ca.row_tok = d_rowtok;
+      ca.rmax = R;
+      ca.Opart = m->Opart;
+      ca.Mpart = m->Mpart;
+      ca.Lpart = m->Lpart;
+      ca.seqs = aa.seqs;
+      ca.row_seq = d_rowseq;
+      ca.R = R;
+      ca.hq = hq;
+      ca.hkv = hkv;
+      ca.dh = dh;
+      ca.scale_log2 = scale_log2;
+      ca.O = m->o;
+      HIPCHK(ks::launch_combine(ca, m->act, st));
+      rc = run_gemm(m, st, m->o, m->qdim, R, W.w_o, m->qdim, D, ks::GEMM_PARTIAL, &splits);
+      if (rc) return rc;
+    } else {
+      int s1 = 1;
+      rc = run_gemm(m, st, m->xa, D, R, W.w_gate_up, D, 2 * d.d_ff, ks::GEMM_SWIGLU, &s1);
+      if (rc) return rc;
+      rc = run_gemm(m, st, m->h, d.d_ff, R, W.w_down, d.d_ff, D, ks::GEMM_PARTIAL, &splits);
+      if (rc) return rc;
+    }
+    ks::ReduceArgs ra{};
+    ra.P = m->P;
+    ra.splits = splits;
+    ra.R = R;
+    ra.d = D;
+    ra.state_old = m->state[0];
+    ra.row_state = d_rowstate;
+    ra.E = m->E;
+    HIPCHK(ks::launch_reduce(ra, st));
+    HIPCHK(ks::launch_carry(m->E, R, D, d.rms_eps, m->state[0], m->xa, m->act, st));
+    return KNAPSPEC_OK;
+  };
+
+  // ---- launches: the draft (gamma steps of the chosen items on one row, each ending with
+  //      the LM head, the greedy token and its embedding), then the verification block
+  HIPCHK(hipMemcpyAsync(dp, hp, upload_bytes, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(x_in, seq->x0, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
+  HIPCHK(ks::launch_carry(seq->x0, 1, D, d.rms_eps, m->state[0], m->xa, m->act, st));
+  HIPCHK(hipEventRecord(ev[0], st));
+  for (int t = 0; t < gamma; ++t) {
+    for (int i = 0; i < L2; ++i) {
+      if (!((mask[i / 64] >> (i % 64)) & 1ull)) continue;
+      int rc = item(i, 1, t, ctx + t);
+      if (rc) return rc;
+    }
+    int rc = run_lm_greedy(m, st, 1);
+    if (rc) return rc;
+    HIPCHK(hipMemcpyAsync(d_tok + t, m->lm_idx, 4, hipMemcpyDeviceToDevice, st));
+    HIPCHK(ks::launch_embed(m->lm_w, m->lm_idx, 1, D, m->act, x_in + (size_t)(t + 1) * D, st));
+    HIPCHK(ks::launch_carry(x_in + (size_t)(t + 1) * D, 1, D, d.rms_eps, m->state[0], m->xa,
+                            m->act, st));
+  }
+  HIPCHK(hipEventRecord(ev[1], st));
+  HIPCHK(ks::launch_carry(x_in, n, D, d.rms_eps, m->state[0], m->xa, m->act, st));
+  for (int i = 0; i < L2; ++i) {
+    int rc = item(i, n, gamma, ctx);
+    if (rc) return rc;
+  }
+  {
+    int rc = run_lm_greedy(m, st, n);
+    if (rc) return rc;
+  }
+  HIPCHK(hipEventRecord(ev[2], st));
+  int32_t* hres = (int32_t*)(hp + o_hres);
+  HIPCHK(hipMemcpyAsync(hres, d_tok, (size_t)gamma * 4, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipMemcpyAsync(hres + gamma, m->lm_idx, (size_t)n * 4, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  float ms0 = 0.f, ms1 = 0.f;
+  HIPCHK(hipEventElapsedTime(&ms0, ev[0], ev[1]));
+  HIPCHK(hipEventElapsedTime(&ms1, ev[1], ev[2]));
+  *draft_us = 1e3 * ms0;
+  *verify_us = 1e3 * ms1;
+  int acc = 0;
+  for (int t = 0; t < gamma; ++t) draft_tokens[t] = hres[t];
+  for (int t = 0; t < n; ++t) verify_tokens[t] = hres[gamma + t];
+  while (acc < gamma && draft_tokens[acc] == verify_tokens[acc]) ++acc;
+  *accepted = acc;
+  return KNAPSPEC_OK;
+}

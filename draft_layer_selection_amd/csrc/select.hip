@@ -669,6 +669,36 @@ __global__ __launch_bounds__(SEL_THREADS) void init_kernel(InitArgs a) {
   }
 }
 
+template <class T>
+__global__ __launch_bounds__(SEL_THREADS) void carry_kernel(const float* src, int d, float eps,
+                                                           float* state, void* xa) {
+  const int t = blockIdx.x;
+  const float* x = src + (size_t)t * d;
+  __shared__ float scratch[SEL_THREADS / 64];
+  const int d4 = d / 4;
+  float ss[1] = {0.f};
+  for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+    const f32x4 v = *(const f32x4*)(x + 4 * e4);
+    *(f32x4*)(state + (size_t)t * d + 4 * e4) = v;
+    ss[0] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  block_sum<1>(ss, scratch);
+  const float scale = 1.0f / sqrtf(ss[0] / (float)d + eps);
+  for (int e4 = threadIdx.x; e4 < d4; e4 += SEL_THREADS) {
+    const f32x4 v = *(const f32x4*)(x + 4 * e4);
+    store_act<T>(xa, t, d, e4, v, scale);
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(SEL_THREADS) void embed_kernel(const T* w, const int* idx, int d,
+                                                           float* out) {
+  const int t = blockIdx.x;
+  const int tok = idx[t];
+  for (int e = threadIdx.x; e < d; e += SEL_THREADS)
+    out[(size_t)t * d + e] = tok >= 0 ? to_f32(w[(size_t)tok * d + e]) : 0.f;
+}
+
 }  // namespace
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
@@ -724,6 +754,32 @@ hipError_t launch_init(const InitArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(init_kernel<float>, grid, block, 0, s, a);
   else
     hipLaunchKernelGGL(init_kernel<bf16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ks
+
+namespace ks {
+
+hipError_t launch_carry(const float* src, int n, int d, float eps, float* state, void* xa,
+                        int act, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (act == ACT_F32)
+    hipLaunchKernelGGL(carry_kernel<float>, dim3(n), dim3(SEL_THREADS), 0, s, src, d, eps, state, xa);
+  else
+    hipLaunchKernelGGL(carry_kernel<bf16>, dim3(n), dim3(SEL_THREADS), 0, s, src, d, eps, state, xa);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const void* w_lm, const int* idx, int n, int d, int act, float* out,
+                        hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (act == ACT_F32)
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(n), dim3(SEL_THREADS), 0, s, (const float*)w_lm,
+                       idx, d, out);
+  else
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(n), dim3(SEL_THREADS), 0, s, (const bf16*)w_lm,
+                       idx, d, out);
   return hipGetLastError();
 }
 

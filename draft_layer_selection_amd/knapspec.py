@@ -27,7 +27,7 @@ KNAPSPEC_BF16 = 1
 KNAPSPEC_RETURN_DECISIONS = 1
 KNAPSPEC_RETURN_MARGINS = 2
 KNAPSPEC_ALPHA_LM_HEAD = 4
-KNAPSPEC_WINDOW_MAX = 8
+KNAPSPEC_WINDOW_MAX = 16
 KNAPSPEC_BEAM_MAX = 8
 KERNEL_CLASSES = ["init", "gemm_qkv", "qkv_rope", "attention", "combine", "gemm_o",
                   "gemm_gate_up", "gemm_down", "select", "lm_head"]
@@ -102,6 +102,11 @@ SIGNATURES = {
                                        C.POINTER(C.c_double), C.POINTER(C.c_double),
                                        C.POINTER(C.c_double)]),
     "knapspec_set_lm_head": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
+    "knapspec_draft_verify": (C.c_int, [C.c_void_p, C.POINTER(knapspec_seq),
+                                        C.POINTER(C.c_uint64), C.c_int32, C.c_void_p,
+                                        C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                        C.POINTER(C.c_int32), C.POINTER(C.c_double),
+                                        C.POINTER(C.c_double)]),
 }
 
 if not os.path.exists(LIB_PATH):
@@ -127,6 +132,7 @@ knapspec_abi_version = lib.knapspec_abi_version
 knapspec_profile_items = lib.knapspec_profile_items
 knapspec_fit_latency = lib.knapspec_fit_latency
 knapspec_set_lm_head = lib.knapspec_set_lm_head
+knapspec_draft_verify = lib.knapspec_draft_verify
 
 
 class KnapSpecError(RuntimeError):
@@ -302,6 +308,24 @@ class Model:
         self._lm_head = w
         _check(knapspec_set_lm_head(self.handle, C.c_void_p(w.data_ptr()), int(vocab)),
                "knapspec_set_lm_head")
+
+    def draft_verify(self, seq: dict, mask: np.ndarray, gamma: int, stream=None):
+        """knapspec_draft_verify: mask uint64 [ceil(2L/64)] -> dict(draft [gamma], verify
+        [gamma+1], accepted, draft_us, verify_us).  Writes seq's caches at ctx .. ctx+gamma."""
+        torch = self._torch
+        carr, keep = self._seq_array([seq])
+        mk = np.ascontiguousarray(mask, dtype=np.uint64)
+        dt = np.zeros(gamma, dtype=np.int32)
+        vt = np.zeros(gamma + 1, dtype=np.int32)
+        acc = C.c_int32()
+        dus, vus = C.c_double(), C.c_double()
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(knapspec_draft_verify(self.handle, carr, _ptr(mk, C.c_uint64), int(gamma),
+                                     C.c_void_p(s), _ptr(dt, C.c_int32), _ptr(vt, C.c_int32),
+                                     C.byref(acc), C.byref(dus), C.byref(vus)),
+               "knapspec_draft_verify")
+        return {"draft": dt, "verify": vt, "accepted": acc.value, "draft_us": dus.value,
+                "verify_us": vus.value}
 
     def set_profiling(self, enable: bool):
         _check(knapspec_set_profiling(self.handle, 1 if enable else 0), "knapspec_set_profiling")

@@ -55,7 +55,7 @@ extern "C" {
 #define KNAPSPEC_RETURN_MARGINS 2   /* fill knapspec_result.margins */
 #define KNAPSPEC_ALPHA_LM_HEAD 4    /* TPT acceptance from the LM head (knapspec_set_lm_head) */
 
-#define KNAPSPEC_WINDOW_MAX 8 /* largest r of an r-token window */
+#define KNAPSPEC_WINDOW_MAX 16 /* largest r of an r-token window */
 #define KNAPSPEC_BEAM_MAX 8   /* largest beam width of the beam variant of the DP */
 
 typedef struct knapspec_model knapspec_model; /* opaque */
@@ -189,6 +189,27 @@ int knapspec_solve(knapspec_model* model, const knapspec_solve_args* args,
  * first call allocates the device buffers the estimate needs (a running argmax per row);
  * EINVAL for a NULL pointer or vocab outside [1, 2^24], ENOMEM when allocation fails. */
 int knapspec_set_lm_head(knapspec_model* model, const void* w, int32_t vocab);
+
+/* One self-speculative step with a chosen layer set, for measuring its speed (review, "The
+ * reading": the draft runs the selected items and the target verifies).  Drafts gamma tokens
+ * greedily through the items whose bit is set in mask (ceil(2L/64) words, bit i = item i),
+ * each token on one row: executed Attention items append the token's key/value to seq's
+ * caches at position ctx_len + t, the LM head gives the greedy token (float32 logits, ties to
+ * the lower index) and its LM-head row is the next token's input (tied embeddings).  Then
+ * verifies: every item on [x0, e(y_0), .., e(y_{gamma-1})] at positions ctx_len .. ctx_len +
+ * gamma as one causal block over the cache 0 .. ctx_len-1 (appending the block's keys/values
+ * at those positions), and the LM head's greedy tokens z_0 .. z_gamma.
+ * seq: x0 is the current token's input [d] (window <= 1); the caches must hold ctx_len +
+ * gamma + 1 positions and are WRITTEN at positions ctx_len .. ctx_len + gamma.  Needs
+ * knapspec_set_lm_head; 1 <= gamma <= KNAPSPEC_WINDOW_MAX - 1.
+ * Outputs (host): draft_tokens[gamma], verify_tokens[gamma + 1], *accepted = the number of
+ * leading t with y_t == z_t, and the device time of the draft and of the verification (HIP
+ * events on hip_stream, microseconds).  Synchronises hip_stream.  Uses the model's workspace
+ * (do not overlap with a solve on the same model). */
+int knapspec_draft_verify(knapspec_model* model, const knapspec_seq* seq, const uint64_t* mask,
+                          int32_t gamma, void* hip_stream, int32_t* draft_tokens,
+                          int32_t* verify_tokens, int32_t* accepted, double* draft_us,
+                          double* verify_us);
 
 /* Host-only TPT grid for caller-supplied acceptance estimates alpha[b] (any a in [0,1]).
  * Ties keep the smaller budget, then the smaller gamma.  Writes -1/-1/NaN when no budget is

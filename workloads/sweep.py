@@ -17,6 +17,11 @@ Experiments the KnapSpec pages describe around the DP, run on seeded synthetic i
   shows the greedy rule's headroom): the same problem solved with the one-state DP and with
   beams of k states per cell; per budget, how much higher the best set's cosine is, and how
   the TPT pick and its value change.
+* Draft/verify timing (review, "The reading": the draft runs the chosen items, the target
+  verifies): the TPT pick (S*, gamma*) run as a masked draft of gamma* tokens and a
+  (gamma*+1)-token verification pass (knapspec_draft_verify), against the same draft with
+  every item (the target decoding token by token).  Speed only: the synthetic weights make
+  acceptance meaningless.
 
 Everything runs through the library (no arithmetic of the method here); this module only
 arranges calls and tabulates what the library returns.  Command line:
@@ -145,6 +150,32 @@ def beam_gap(prob, beams: Sequence[int], reps: int = 3, band: Optional[float] = 
     return rows
 
 
+def draft_verify_timing(prob, reps: int = 3) -> dict:
+    """Device time of the TPT pick's masked draft and of its verification, and of a draft with
+    every item executed, at the preset context (median of reps after one warm-up call).
+    The caches must hold ctx + gamma* + 1 positions; positions ctx .. ctx+gamma* are written."""
+    wl = prob.wl
+    n_items = 2 * wl.shape.n_layers
+    res = prob.solve()
+    b, g = int(res.best_budget[0]), int(res.best_gamma[0])
+    g = max(1, min(g, prob.ks.KNAPSPEC_WINDOW_MAX - 1))
+    mw = (n_items + 63) // 64
+    full = np.zeros(mw, dtype=np.uint64)
+    for i in range(n_items):
+        full[i // 64] |= np.uint64(1) << np.uint64(i % 64)
+    out = {"pick_budget": b, "gamma": g,
+           "pick_items": int(_mask_bits(res.masks[0][b:b + 1], n_items).sum()) if b >= 0 else 0,
+           "t_draft_model": float(res.t_draft[0][b]) if b >= 0 else None}
+    seq = prob.seq_args()[0]
+    for name, mask in (("pick", res.masks[0][b] if b >= 0 else full), ("full", full)):
+        prob.model.draft_verify(seq, mask, g)  # warm-up
+        runs = [prob.model.draft_verify(seq, mask, g) for _ in range(reps)]
+        out[f"{name}_draft_us"] = float(np.median([r["draft_us"] for r in runs]))
+        out[f"{name}_verify_us"] = float(np.median([r["verify_us"] for r in runs]))
+        out[f"{name}_draft_us_per_token"] = out[f"{name}_draft_us"] / g
+    return out
+
+
 def latency_profile(prob, ctx_list: Sequence[int], reps: int = 8) -> dict:
     """Measured item latencies and the fitted linear attention model (microseconds)."""
     seq = prob.seq_args([max(ctx_list)])[0]
@@ -163,6 +194,8 @@ def main(argv=None):
     ap.add_argument("--taus", default="-inf,0.0,0.3,0.5,0.7,0.9")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--beams", default="", help="beam widths for the beam-gap table, e.g. 1,2,4,8")
+    ap.add_argument("--draft-verify", type=int, default=0, metavar="VOCAB",
+                    help="time the pick's masked draft + verification with an LM head of VOCAB rows")
     ap.add_argument("--profiled", action="store_true",
                     help="also solve the sweep with the measured (fitted) latency model")
     ap.add_argument("--seed", type=int, default=0)
@@ -176,10 +209,10 @@ def main(argv=None):
         wl = scaled(wl, n_layers=args.layers)
     ctx_list = [int(x) for x in args.ctx.split(",")]
     taus = [float(x) for x in args.taus.split(",")]
-    cap = max(max(ctx_list), wl.ctx)
+    cap = max(max(ctx_list), wl.ctx) + 16  # room for a draft/verify block past the context
     beams = [int(x) for x in args.beams.split(",")] if args.beams else []
     prob = DeviceProblem(wl, args.seed, ctxs=[wl.ctx], caps=[cap],
-                         max_beam=max(beams) if beams else 1)
+                         max_beam=max(beams) if beams else 1, lm_vocab=args.draft_verify)
     out = {"workload": wl.name, "layers": wl.shape.n_layers, "n_budgets": wl.n_budgets,
            "latency_model": "bandwidth-bound stand-in (8 TB/s)",
            "sweep": context_sweep(prob, ctx_list)}
@@ -189,6 +222,9 @@ def main(argv=None):
     if beams:
         out["beam_gap"] = beam_gap(prob, beams, reps=args.reps)
         print(json.dumps({"beam_gap": out["beam_gap"]}), flush=True)
+    if args.draft_verify:
+        out["draft_verify"] = draft_verify_timing(prob, reps=args.reps)
+        print(json.dumps({"draft_verify": out["draft_verify"]}), flush=True)
     if len(set(ctx_list)) < 2:  # a line fit needs two context lengths
         prob.close()
         if args.out:
