@@ -208,7 +208,17 @@ struct knapspec_model {
   size_t pr_bytes = 0;
   hipEvent_t pr_ev[2] = {nullptr, nullptr};
 
+  // masked draft / verification (knapspec_draft_verify): timing events and a captured graph
+  // of the last repeated configuration
+  hipEvent_t dv_ev[3] = {nullptr, nullptr, nullptr};
+  hipGraphExec_t dv_gexec[2] = {nullptr, nullptr};  // draft phase, verification phase
+  std::vector<int64_t> dv_key, dv_last_key;
+
   ~knapspec_model() {
+    for (hipEvent_t e : dv_ev)
+      if (e) (void)hipEventDestroy(e);
+    for (hipGraphExec_t g : dv_gexec)
+      if (g) (void)hipGraphExecDestroy(g);
     for (hipEvent_t e : pr_ev)
       if (e) (void)hipEventDestroy(e);
     if (pr_dev) (void)hipFree(pr_dev);
@@ -1729,22 +1739,14 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
         for (int qb = 0; qb < qbs; ++qb) work[nw++] = make_int4(0, cc, qb, sp);
     nwork[k] = nw;
   }
-  hipStream_t st = (hipStream_t)hip_stream;
-  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-  for (auto& e : ev)
-    if (hipEventCreate(&e) != hipSuccess) {
+  hipStream_t st = nullptr;  // the stream the launches below go to (set before enqueueing)
+  for (auto& e : m->dv_ev)
+    if (!e && hipEventCreate(&e) != hipSuccess) {
       (void)hipGetLastError();
-      for (auto& f : ev)
-        if (f) (void)hipEventDestroy(f);
+      e = nullptr;
       return fail(KNAPSPEC_EHIP, "event creation failed");
     }
-  struct EvGuard {
-    hipEvent_t* e;
-    ~EvGuard() {
-      for (int i = 0; i < 3; ++i)
-        if (e[i]) (void)hipEventDestroy(e[i]);
-    }
-  } guard{ev};
+  hipEvent_t* ev = m->dv_ev;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   const int32_t* d_rowseq = (const int32_t*)(dp + o_rowseq);
   const int32_t* d_rowstate = (const int32_t*)(dp + o_rowstate);
@@ -1835,10 +1837,14 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
 
   // ---- launches: the draft (gamma steps of the chosen items on one row, each ending with
   //      the LM head, the greedy token and its embedding), then the verification block
+  int32_t* hres = (int32_t*)(hp + o_hres);
+  // phase 0: upload, the draft; phase 1: the verification and the result copies.  Timing
+  // events are recorded between the phases (outside any captured graph).
+  auto enqueue = [&](int phase) -> int {
+  if (phase == 0) {
   HIPCHK(hipMemcpyAsync(dp, hp, upload_bytes, hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(x_in, seq->x0, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
   HIPCHK(ks::launch_carry(seq->x0, 1, D, d.rms_eps, m->state[0], m->xa, m->act, st));
-  HIPCHK(hipEventRecord(ev[0], st));
   for (int t = 0; t < gamma; ++t) {
     for (int i = 0; i < L2; ++i) {
       if (!((mask[i / 64] >> (i % 64)) & 1ull)) continue;
@@ -1852,7 +1858,8 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
     HIPCHK(ks::launch_carry(x_in + (size_t)(t + 1) * D, 1, D, d.rms_eps, m->state[0], m->xa,
                             m->act, st));
   }
-  HIPCHK(hipEventRecord(ev[1], st));
+  return KNAPSPEC_OK;
+  }
   HIPCHK(ks::launch_carry(x_in, n, D, d.rms_eps, m->state[0], m->xa, m->act, st));
   for (int i = 0; i < L2; ++i) {
     int rc = item(i, n, gamma, ctx);
@@ -1862,11 +1869,79 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
     int rc = run_lm_greedy(m, st, n);
     if (rc) return rc;
   }
-  HIPCHK(hipEventRecord(ev[2], st));
-  int32_t* hres = (int32_t*)(hp + o_hres);
   HIPCHK(hipMemcpyAsync(hres, d_tok, (size_t)gamma * 4, hipMemcpyDeviceToHost, st));
   HIPCHK(hipMemcpyAsync(hres + gamma, m->lm_idx, (size_t)n * 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(hipStreamSynchronize(st));
+  return KNAPSPEC_OK;
+  };
+
+  // ---- run: like a solve, replay a captured graph when the configuration (layer set, gamma,
+  //      context, buffers) is the one captured last; capture it the second time in a row
+  hipStream_t caller = (hipStream_t)hip_stream;
+  const char* genv = std::getenv("KNAPSPEC_GRAPHS");
+  const bool graphs = !(genv && genv[0] == '0') && m->own_stream;
+  if (!graphs) {
+    st = caller;
+    for (int ph = 0; ph < 2; ++ph) {
+      HIPCHK(hipEventRecord(ev[ph], st));
+      int rc = enqueue(ph);
+      if (rc) return rc;
+    }
+    HIPCHK(hipEventRecord(ev[2], st));
+    HIPCHK(hipStreamSynchronize(caller));
+  } else {
+    std::vector<int64_t> key = {gamma, ctx, seq->ctx_capacity, (int64_t)(intptr_t)seq->x0,
+                                (int64_t)(intptr_t)m->lm_w, m->lm_vocab,
+                                (int64_t)(intptr_t)dp, (int64_t)(intptr_t)hp};
+    for (int wd = 0; wd < m->mw; ++wd) key.push_back((int64_t)mask[wd]);
+    for (int l = 0; l < nl; ++l) {
+      key.push_back((int64_t)(intptr_t)seq->k_cache[l]);
+      key.push_back((int64_t)(intptr_t)seq->v_cache[l]);
+    }
+    st = m->own_stream;
+    HIPCHK(hipEventRecord(m->ev_in, caller));
+    HIPCHK(hipStreamWaitEvent(st, m->ev_in, 0));
+    const bool replay = m->dv_gexec[0] && m->dv_gexec[1] && key == m->dv_key;
+    const bool capture = !replay && key == m->dv_last_key;
+    m->dv_last_key = key;
+    if (capture) {
+      for (hipGraphExec_t& g : m->dv_gexec)
+        if (g) {
+          (void)hipGraphExecDestroy(g);
+          g = nullptr;
+        }
+      m->dv_key.clear();
+      for (int ph = 0; ph < 2; ++ph) {
+        HIPCHK(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+        const int rc = enqueue(ph);
+        hipGraph_t graph = nullptr;
+        const hipError_t ec = hipStreamEndCapture(st, &graph);
+        if (rc) {
+          if (graph) (void)hipGraphDestroy(graph);
+          return rc;
+        }
+        if (ec != hipSuccess || !graph)
+          return fail(KNAPSPEC_EHIP, "graph capture failed: %s", hipGetErrorString(ec));
+        const hipError_t ei = hipGraphInstantiate(&m->dv_gexec[ph], graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (ei != hipSuccess) {
+          m->dv_gexec[ph] = nullptr;
+          return fail(KNAPSPEC_EHIP, "graph instantiation failed: %s", hipGetErrorString(ei));
+        }
+      }
+      m->dv_key = key;
+    }
+    for (int ph = 0; ph < 2; ++ph) {
+      HIPCHK(hipEventRecord(ev[ph], st));
+      if (replay || capture) {
+        HIPCHK(hipGraphLaunch(m->dv_gexec[ph], st));
+      } else {
+        int rc = enqueue(ph);
+        if (rc) return rc;
+      }
+    }
+    HIPCHK(hipEventRecord(ev[2], st));
+    HIPCHK(hipStreamSynchronize(st));
+  }
   float ms0 = 0.f, ms1 = 0.f;
   HIPCHK(hipEventElapsedTime(&ms0, ev[0], ev[1]));
   HIPCHK(hipEventElapsedTime(&ms1, ev[1], ev[2]));
