@@ -226,10 +226,13 @@ def ko_weights(wl, ctx):
     return [max(1, int(round(x / delta))) for x in t]
 
 
-def cpu_baseline(wl, prob, sample_layers, log_fn):
-    """The oracle, untuned, on a bounded prefix of the same solve: the first
-    ``sample_layers`` layers (2 items each) of the DP over the same inputs.  The rate is scaled
-    to whole solves by the fraction of the solve's FLOPs that prefix holds."""
+def cpu_baseline(wl, prob, max_layers, log_fn, seconds=15.0):
+    """The oracle, untuned, on a bounded prefix of the same solve: the DP over the same inputs,
+    stopped at the first item boundary after ``seconds`` of wall time (or after ``max_layers``
+    layers).  The oracle runs unchanged; a wrapper around its item function only reads the
+    clock when the next item starts, so the timed prefix holds whole items (their forward and
+    their select).  The rate is scaled to whole solves by the fraction of the solve's FLOPs
+    the finished items hold."""
     import numpy as np
 
     from oracle import knapspec_oracle as ko
@@ -241,12 +244,28 @@ def cpu_baseline(wl, prob, sample_layers, log_fn):
     t = ko.item_latencies(s.n_layers, prob.ctxs[0], lat.attn_base, lat.attn_per_token, lat.mlp)
     w = ko.item_weights(t, wl.n_budgets)
     items = ko.DecoderItems(shape, prob.host_layers, prob.host_kv[0], prob.ctxs[0])
-    n_items = 2 * sample_layers
+    n_max = 2 * min(max_layers, s.n_layers)
+
+    class _Stop(Exception):
+        pass
+
     t0 = time.perf_counter()
-    ko.knapsack_dp(items, n_items, w[:n_items], prob.host_x0[0], wl.n_budgets)
-    dt = time.perf_counter() - t0
-    cls, tot = algorithmic_work(wl, [w], prob.ctxs[:1])
-    # FLOP share of the sampled prefix
+    mark = {"done": 0, "t": 0.0}
+
+    def timed(i, x):
+        now = time.perf_counter() - t0
+        mark["done"], mark["t"] = i, now  # items 0 .. i-1 are finished
+        if i > 0 and now >= seconds:
+            raise _Stop
+        return items(i, x)
+
+    try:
+        ko.knapsack_dp(timed, n_max, w[:n_max], prob.host_x0[0], wl.n_budgets)
+        mark["done"], mark["t"] = n_max, time.perf_counter() - t0
+    except _Stop:
+        pass
+    n_items, dt = mark["done"], mark["t"]
+    # FLOP share of the finished prefix
     rows, _ = item_rows(list(w), wl.n_budgets)
     d, ff, dh, hq, hkv = s.d_model, s.d_ff, s.head_dim, s.n_q_heads, s.n_kv_heads
     qd, nqkv = hq * dh, (hq + 2 * hkv) * dh
@@ -259,8 +278,9 @@ def cpu_baseline(wl, prob, sample_layers, log_fn):
     threads = len(os.sched_getaffinity(0))
     log_fn(f"[cpu] oracle {n_items} items in {dt:.2f}s = {frac:.3%} of one solve's FLOPs")
     return {"value": frac / dt, "unit": "solves/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {sample_layers} of {s.n_layers} layers ({n_items} items) of one "
-                      f"{wl.name} solve, {dt:.1f}s; scaled by its FLOP share {frac:.4f}"}
+            "sample": f"first {n_items} of {2 * s.n_layers} items of one {wl.name} solve "
+                      f"(stopped at the first item boundary after {seconds:g} s), {dt:.1f}s; "
+                      f"scaled by its FLOP share {frac:.4f}"}
 
 
 def main():
@@ -271,7 +291,8 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=20)
+    ap.add_argument("--cpu-layers", type=int, default=1000)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--summarize-profiles", action="store_true")
     ap.add_argument("--stats")
@@ -412,7 +433,7 @@ def main():
     cpu = None
     if want_cpu:
         try:
-            cpu = cpu_baseline(wl, prob, args.cpu_layers, log)
+            cpu = cpu_baseline(wl, prob, args.cpu_layers, log, args.cpu_seconds)
         except Exception as e:  # the baseline is reported, never required for the GPU number
             log(f"[cpu] baseline failed: {e!r}")
     line = {
