@@ -210,10 +210,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int nq = G * S.M;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int t = qb * QB + wave * 32 + l32;
-  const bool tvalid = t < nq;
-  // a wave whose 32 query rows are all past the end only helps stage the tiles
-  const bool wactive = qb * QB + wave * 32 < nq;
+  // block qb holds query rows [qb*qbr, qb*qbr + qbr) of the KV head; a wave whose 32 rows are
+  // outside the block or all past the end only helps stage the tiles
+  const int qbr = S.qrows > 0 ? S.qrows : QB;
+  const int t = qb * qbr + wave * 32 + l32;
+  const bool wactive = wave * 32 < qbr && qb * qbr + wave * 32 < nq;
+  const bool tvalid = wactive && t < nq;
   const int tt = tvalid ? t : nq - 1;
   const int row = S.row_off + tt / G;
   const int h = c * G + tt % G;

@@ -15,6 +15,9 @@
 //     wave issues the same number of loads per stage and the tail re-issues the last stage, so
 //     the wait count is a compile-time constant and the loop carries no per-stage branches
 //     (branchy per-stage bookkeeping cost ~15-20% at large R, measured);
+//   * MFMA operands are double-buffered in registers: the LDS reads of the next 16-wide K step
+//     alternate with the MFMAs of the current one (order pinned with sched_group_barrier), and
+//     the barrier opening the next stage sits after the first MFMAs of a stage's last K step;
 //   * activations are re-read from L2 once per column tile, i.e. R/(64*NG) times the weight
 //     bytes, so the planner widens the tile (NG=4) when R > 128;
 //   * K-slice partial sums are reduced through LDS in a fixed order (deterministic); K is split
@@ -269,43 +272,104 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
   for (int p = 0; p < S - 1; ++p) issue(min(p, nit - 1), p);
 
-  // one 64-K stage; slot J is a compile-time constant (the loop below is unrolled by S), so
-  // the LDS addresses are per-lane registers plus immediates
-  auto stage = [&](auto Jc, int it) {
-    constexpr int J = decltype(Jc)::value;
-    wait_vm_const<(S - 2) * PER_WAVE>();  // this wave's part of stage `it` landed
-    asm volatile("s_barrier" ::: "memory");  // ... and everyone else's
-    issue(min(it + S - 1, nit - 1), (J + S - 1) % S);  // refill the slot freed above
-    const unsigned char* st = smem + J * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int c = 2 * (ksl * KSTEPS + ks) + hi;  // 16-byte chunk of this lane's K
-      bf16x8 wf[2], af[MB];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int r = 64 * grp + 32 * cb + l32;
-        wf[cb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = WR + 32 * mb + l32;
-        af[mb] = *(const bf16x8*)(st + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], wf[0], acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], wf[1], acc[mb][1], 0, 0, 0);
-      }
-    }
+  // Software pipeline over the 16-wide K steps: two register buffers of MFMA operands; the
+  // operands of the next K step are read from LDS while the MFMAs of the current one run
+  // (reads and MFMAs alternate), so the MFMA pipe does not wait for LDS latency.  The barrier
+  // that opens stage it+1 is taken inside the last K step of stage it, after its first MFMAs:
+  // every operand of stage it is in registers by then, so the refill of its slot is safe, and
+  // the MFMAs in flight cover the barrier.  Slot and buffer indices are compile-time constants
+  // (the loop is unrolled by U stages), so LDS addresses are immediates and the compiler can
+  // tell the DMA targets from the slots being read.
+  bf16x8 wf[2][2], af[2][MB];
+  auto read_w = [&](auto Jc, auto ksc, auto bc, auto cbc) {
+    constexpr int J = decltype(Jc)::value, ks = decltype(ksc)::value;
+    constexpr int b = decltype(bc)::value, cb = decltype(cbc)::value;
+    const int c = 2 * (ksl * KSTEPS + ks) + hi;
+    const int r = 64 * grp + 32 * cb + l32;
+    wf[b][cb] = *(const bf16x8*)(smem + J * STAGE + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
   };
-  // whole rounds of S stages without conditions (the compiler then tracks the outstanding
-  // loads exactly), then the remainder
+  auto read_a = [&](auto Jc, auto ksc, auto bc, auto mbc) {
+    constexpr int J = decltype(Jc)::value, ks = decltype(ksc)::value;
+    constexpr int b = decltype(bc)::value, mb = decltype(mbc)::value;
+    const int c = 2 * (ksl * KSTEPS + ks) + hi;
+    const int r = WR + 32 * mb + l32;
+    af[b][mb] = *(const bf16x8*)(smem + J * STAGE + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
+  };
+  // operand read number q (0 .. MB+1) of K step (J, ks) into buffer b, in the order the
+  // MFMAs below first use them: W0, A0, W1, A1, A2, ...
+  auto read_op = [&](auto Jc, auto ksc, auto bc, auto qc) {
+    constexpr int q = decltype(qc)::value;
+    if constexpr (q == 0 || q == 2)
+      read_w(Jc, ksc, bc, std::integral_constant<int, q / 2>{});
+    else
+      read_a(Jc, ksc, bc, std::integral_constant<int, q == 1 ? 0 : q - 2>{});
+  };
+  // MFMA number m (0 .. 2MB-1) of the K step held in buffer b
+  auto mfma = [&](auto bc, auto mc) {
+    constexpr int b = decltype(bc)::value, m = decltype(mc)::value;
+    constexpr int mb = m / 2, cb = m % 2;
+    acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][mb], wf[b][cb], acc[mb][cb], 0, 0, 0);
+  };
+  constexpr int NM = 2 * MB, NR = MB + 2;
+  // MFMAs first .. NM-1 of buffer b alternating with the NR reads of the next K step, in a
+  // scheduling region of its own whose order is pinned (MFMA, LDS read, MFMA, ...): left to
+  // itself the scheduler groups the reads after the MFMAs and waits for each group.
+  auto interleave = [&](auto bc, auto firstc, auto nJc, auto nksc) {
+    constexpr int b = decltype(bc)::value, first = decltype(firstc)::value;
+    constexpr int n = NM - first > NR ? NM - first : NR;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<n>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (first + i < NM) mfma(bc, std::integral_constant<int, first + i>{});
+      if constexpr (i < NR)
+        read_op(nJc, nksc, std::integral_constant<int, 1 - b>{}, std::integral_constant<int, i>{});
+    });
+    static_for<n>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (first + i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int EARLY = 2 * MB - (MB + 2) > 1 ? 2 * MB - (MB + 2) : 1;  // MFMAs before the barrier
+  // one stage (slot J, local index Jl within the unrolled group), stage number it
+  auto stage = [&](auto Jlc, int it) {
+    constexpr int Jl = decltype(Jlc)::value, J = Jl % S, Jn = (Jl + 1) % S;
+    static_for<KSTEPS>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      constexpr int b = (Jl * KSTEPS + ks) & 1;
+      using B = std::integral_constant<int, b>;
+      if constexpr (ks + 1 < KSTEPS) {
+        interleave(B{}, std::integral_constant<int, 0>{}, std::integral_constant<int, J>{},
+                   std::integral_constant<int, ks + 1>{});
+      } else {
+        static_for<EARLY>([&](auto mc) { mfma(B{}, mc); });
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_const<(S - 2) * PER_WAVE>();  // this wave's part of stage it+1 landed
+        asm volatile("s_barrier" ::: "memory");  // ... and everyone else's; slot J is read out
+        issue(min(it + S, nit - 1), J);         // refill it with stage it+S
+        __builtin_amdgcn_sched_barrier(0);
+        interleave(B{}, std::integral_constant<int, EARLY>{}, std::integral_constant<int, Jn>{},
+                   std::integral_constant<int, 0>{});
+      }
+    });
+  };
+  // unroll by U stages: a multiple of S (compile-time slots) with an even number of K steps
+  // (compile-time buffer parity)
+  constexpr int U = (S * KSTEPS) % 2 == 0 ? S : 2 * S;
+  wait_vm_const<(S - 2) * PER_WAVE>();  // stage 0
+  asm volatile("s_barrier" ::: "memory");
+  issue(min(S - 1, nit - 1), S - 1);  // the last slot, unused so far
+  static_for<NR>([&](auto qc) {
+    read_op(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+            std::integral_constant<int, 0>{}, qc);
+  });
   int it0 = 0;
-  for (; it0 + S <= nit; it0 += S)
-    static_for<S>([&](auto Jc) { stage(Jc, it0 + decltype(Jc)::value); });
-  static_for<S>([&](auto Jc) {
-    constexpr int J = decltype(Jc)::value;
-    if (it0 + J < nit) stage(Jc, it0 + J);
+  for (; it0 + U <= nit; it0 += U)
+    static_for<U>([&](auto Jlc) { stage(Jlc, it0 + decltype(Jlc)::value); });
+  static_for<U>([&](auto Jlc) {
+    constexpr int Jl = decltype(Jlc)::value;
+    if (it0 + Jl < nit) stage(Jlc, it0 + Jl);
   });
   wait_vm_const<0>();  // repeated tail loads may still be writing the ring the reduction reuses
   __syncthreads();

@@ -62,7 +62,10 @@ struct AttnSeq {
   int chunk;      // positions per split (multiple of 64)
   int part_off;   // first partial slot of the sequence; slot of (split sp, local row r,
                   // head h) = part_off + (sp * M + r) * hq + h
-  int pad0, pad1, pad2;
+  int pad0;
+  int qrows;      // query rows per workgroup of the bf16 MFMA kernel (multiple of 32, at most
+                  // 256; 0 = 256): a KV head's G*M query rows are spread evenly over its blocks
+  int pad2;
 };
 
 // Partial-result slot of one (split, row, query head) of a sequence.

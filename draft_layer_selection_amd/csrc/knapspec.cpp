@@ -94,6 +94,15 @@ MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int
 // part_cap partial slots.
 constexpr long ATTN_WG_FIXED_TILES = 4;  // pipeline fill + the partial-result write of a
                                          // workgroup (256 rows x 512 B ~ 4 tiles of traffic)
+// Query rows per block when a KV head's nq query rows are spread over nblk blocks: the
+// smallest multiple of 32 with nblk blocks covering nq (the last block is then at most 32 rows
+// shorter than the others, instead of holding the remainder of full blocks).
+int balanced_qrows(int nq, int nblk) {
+  if (nblk <= 0) return 0;
+  const int per = (nq + nblk - 1) / nblk;
+  return (per + 31) / 32 * 32;
+}
+
 void plan_attention_splits(const std::vector<int>& pairs, const std::vector<int>& tiles,
                            const std::vector<size_t>& rows, int slots, int max_split,
                            size_t part_cap, std::vector<int>& nsplit) {
@@ -844,7 +853,8 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
         as.chunk = chunk;
         as.part_off = (int)part;
         as.pad0 = win[q];
-        as.pad1 = as.pad2 = 0;
+        as.qrows = balanced_qrows(G * M, qblocks[q]);
+        as.pad2 = 0;
         part += (size_t)as.nsplit * M * hq;
         for (int c = 0; c < hkv; ++c)
           for (int sp = 0; sp < as.nsplit; ++sp) {
@@ -1727,6 +1737,7 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
     as.chunk = chunk;
     as.part_off = 0;
     as.pad0 = M;
+    as.qrows = balanced_qrows(G * M, qbs);
     for (int l = 0; l < nl; ++l) {
       as.k = seq->k_cache[l];
       as.v = seq->v_cache[l];
