@@ -498,40 +498,83 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_floats) {
   GemmPlan p{};
   const int ncols = mode == GEMM_SWIGLU ? 2 * ff : N;
+  const int kstep = act == ACT_F32 ? 32 : 64;
+  const int kiters = (K + kstep - 1) / kstep;
+  auto finish = [&](int s) {
+    const int per = (kiters + s - 1) / s;
+    p.k_chunk = per * kstep;
+    p.splits = (kiters + per - 1) / per;
+  };
   if (act == ACT_F32) {
     p.ng = 0;
     p.mb = 1;
     p.m_tiles = (R + 31) / 32;
     p.n_tiles = mode == GEMM_SWIGLU ? (ff + 31) / 32 : (N + 63) / 64;
-  } else {
-    p.m_tiles = (R + 127) / 128;
-    p.mb = (R + 32 * p.m_tiles - 1) / (32 * p.m_tiles);
-    const bool k_ok = K % 64 == 0;
-    if (k_ok && R > 128 && ncols % 256 == 0 && (mode != GEMM_SWIGLU || ff % 128 == 0))
-      p.ng = 4;
-    else if (k_ok && ncols % 128 == 0 && (mode != GEMM_SWIGLU || ff % 64 == 0))
-      p.ng = 2;
-    else
-      p.ng = 0;
-    const int cols = p.ng ? 64 * p.ng : 64;
-    p.n_tiles = mode == GEMM_SWIGLU ? ff / (cols / 2) : N / cols;
+    int s = 1;
+    if (mode != GEMM_SWIGLU) {
+      s = std::max(1, 512 / std::max(1, p.n_tiles * p.m_tiles));
+      s = std::min(std::min(s, 16), std::max(1, kiters / 4));
+      while (s > 1 && (size_t)s * R * N > cap_floats) --s;
+    }
+    finish(s);
+    return p;
   }
-  const int kstep = act == ACT_F32 ? 32 : 64;
-  const int kiters = (K + kstep - 1) / kstep;
+  const bool k_ok = K % 64 == 0;
+  if (mode == GEMM_PARTIAL && k_ok && N % 128 == 0) {
+    // K-split LDS kernel: pick the tile (64*ng columns x 32*mb rows) and split count with the
+    // least modelled time: rounds of 256 workgroups x bytes each workgroup stages through LDS
+    // (its K stages plus 2 stages' worth of start-up), plus the fp32 partial sums written and
+    // read back (weighted 0.01 per byte).  The split count is capped at K/(4R), which keeps the
+    // partial traffic within 2x the weight bytes where the rows are many; 256-column tiles
+    // only above 128 rows.  Fitted to cold-weight timings of the Llama-3-8B shapes (q|k|v, O
+    // and down projections, R = 32 .. 245, GEMM plus split reduction): within 2% of the best
+    // tile and split count per shape, against 5% for a fixed 256-workgroup target.
+    const int smax = std::max(1, std::min(16, K / std::max(1, 4 * R)));
+    double best = -1;
+    for (int ng : {2, 4}) {
+      if (ng == 4 && (N % 256 != 0 || R <= 128)) continue;
+      for (int mb = 1; mb <= 4; ++mb) {
+        const int mt = (R + 32 * mb - 1) / (32 * mb), nt = N / (64 * ng), tiles = mt * nt;
+        int s = std::min(smax, tiles < 256 ? 256 / tiles : 1);
+        s = std::max(1, std::min(s, std::max(1, kiters / 4)));
+        while (s > 1 && (size_t)s * R * N > cap_floats) --s;
+        const int per = (kiters + s - 1) / s;
+        s = (kiters + per - 1) / per;
+        const double rounds = (double)((mt * nt * s + 255) / 256);
+        const double t = rounds * (64.0 * ng + 32.0 * mb) * 128.0 * (per + 2) +
+                         0.01 * (double)s * R * N * 8.0;
+        if (best < 0 || t < best) {
+          best = t;
+          p.ng = ng;
+          p.mb = mb;
+          p.m_tiles = mt;
+          p.n_tiles = nt;
+          p.k_chunk = per * 64;
+          p.splits = s;
+        }
+      }
+    }
+    return p;
+  }
+  p.m_tiles = (R + 127) / 128;
+  p.mb = (R + 32 * p.m_tiles - 1) / (32 * p.m_tiles);
+  if (k_ok && R > 128 && ncols % 256 == 0 && (mode != GEMM_SWIGLU || ff % 128 == 0))
+    p.ng = 4;
+  else if (k_ok && ncols % 128 == 0 && (mode != GEMM_SWIGLU || ff % 64 == 0))
+    p.ng = 2;
+  else
+    p.ng = 0;
+  const int cols = p.ng ? 64 * p.ng : 64;
+  p.n_tiles = mode == GEMM_SWIGLU ? ff / (cols / 2) : N / cols;
   int s = 1;
   if (mode != GEMM_SWIGLU) {
+    // direct-load fallback kernel (N not a multiple of 128 or K of 64)
     const int tiles = p.n_tiles * p.m_tiles;
-    const int lds_kernel = p.ng != 0;
-    // one workgroup per CU for the LDS kernel: fill up to 256 without a second round
-    const int target = lds_kernel ? 256 : 512;
-    s = std::max(1, target / std::max(1, tiles));
-    s = std::min(s, 16);
-    s = std::min(s, std::max(1, kiters / 4));
+    s = std::max(1, 512 / std::max(1, tiles));
+    s = std::min(std::min(s, 16), std::max(1, kiters / 4));
     while (s > 1 && (size_t)s * R * N > cap_floats) --s;
   }
-  const int per = (kiters + s - 1) / s;
-  p.k_chunk = per * kstep;
-  p.splits = (kiters + per - 1) / per;
+  finish(s);
   return p;
 }
 
