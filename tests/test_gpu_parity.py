@@ -85,6 +85,14 @@ def test_bf16_small_mfma_path():
     run_case(wl, ctxs=[1000], n_budgets=64)
 
 
+def test_bf16_several_query_blocks():
+    # GQA group of 4 with up to 116 rows per attention item: a KV head's 4*M query rows span
+    # two 256-row blocks from M = 65 on, spread evenly over them (e.g. 260 rows as 160 + 100)
+    wl = scaled(WORKLOADS["llama3_8b_32k"], n_layers=12, d_model=1024, n_q_heads=8,
+                n_kv_heads=2, d_ff=2048, name="llama_like_qblocks")
+    run_case(wl, ctxs=[300], n_budgets=128)
+
+
 def test_bf16_head_dim_64():
     wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=3, d_model=512, n_q_heads=8,
                 n_kv_heads=2, head_dim=64, d_ff=1024, name="bf16_dh64")
