@@ -1852,37 +1852,36 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
   // phase 0: upload, the draft; phase 1: the verification and the result copies.  Timing
   // events are recorded between the phases (outside any captured graph).
   auto enqueue = [&](int phase) -> int {
-  if (phase == 0) {
-  HIPCHK(hipMemcpyAsync(dp, hp, upload_bytes, hipMemcpyHostToDevice, st));
-  HIPCHK(hipMemcpyAsync(x_in, seq->x0, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
-  HIPCHK(ks::launch_carry(seq->x0, 1, D, d.rms_eps, m->state[0], m->xa, m->act, st));
-  for (int t = 0; t < gamma; ++t) {
+    if (phase == 0) {
+      HIPCHK(hipMemcpyAsync(dp, hp, upload_bytes, hipMemcpyHostToDevice, st));
+      HIPCHK(hipMemcpyAsync(x_in, seq->x0, (size_t)D * 4, hipMemcpyDeviceToDevice, st));
+      HIPCHK(ks::launch_carry(seq->x0, 1, D, d.rms_eps, m->state[0], m->xa, m->act, st));
+      for (int t = 0; t < gamma; ++t) {
+        for (int i = 0; i < L2; ++i) {
+          if (!((mask[i / 64] >> (i % 64)) & 1ull)) continue;
+          const int rc = item(i, 1, t, ctx + t);
+          if (rc) return rc;
+        }
+        const int rc = run_lm_greedy(m, st, 1);
+        if (rc) return rc;
+        HIPCHK(hipMemcpyAsync(d_tok + t, m->lm_idx, 4, hipMemcpyDeviceToDevice, st));
+        HIPCHK(ks::launch_embed(m->lm_w, m->lm_idx, 1, D, m->act, x_in + (size_t)(t + 1) * D,
+                                st));
+        HIPCHK(ks::launch_carry(x_in + (size_t)(t + 1) * D, 1, D, d.rms_eps, m->state[0],
+                                m->xa, m->act, st));
+      }
+      return KNAPSPEC_OK;
+    }
+    HIPCHK(ks::launch_carry(x_in, n, D, d.rms_eps, m->state[0], m->xa, m->act, st));
     for (int i = 0; i < L2; ++i) {
-      if (!((mask[i / 64] >> (i % 64)) & 1ull)) continue;
-      int rc = item(i, 1, t, ctx + t);
+      const int rc = item(i, n, gamma, ctx);
       if (rc) return rc;
     }
-    int rc = run_lm_greedy(m, st, 1);
+    const int rc = run_lm_greedy(m, st, n);
     if (rc) return rc;
-    HIPCHK(hipMemcpyAsync(d_tok + t, m->lm_idx, 4, hipMemcpyDeviceToDevice, st));
-    HIPCHK(ks::launch_embed(m->lm_w, m->lm_idx, 1, D, m->act, x_in + (size_t)(t + 1) * D, st));
-    HIPCHK(ks::launch_carry(x_in + (size_t)(t + 1) * D, 1, D, d.rms_eps, m->state[0], m->xa,
-                            m->act, st));
-  }
-  return KNAPSPEC_OK;
-  }
-  HIPCHK(ks::launch_carry(x_in, n, D, d.rms_eps, m->state[0], m->xa, m->act, st));
-  for (int i = 0; i < L2; ++i) {
-    int rc = item(i, n, gamma, ctx);
-    if (rc) return rc;
-  }
-  {
-    int rc = run_lm_greedy(m, st, n);
-    if (rc) return rc;
-  }
-  HIPCHK(hipMemcpyAsync(hres, d_tok, (size_t)gamma * 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(hipMemcpyAsync(hres + gamma, m->lm_idx, (size_t)n * 4, hipMemcpyDeviceToHost, st));
-  return KNAPSPEC_OK;
+    HIPCHK(hipMemcpyAsync(hres, d_tok, (size_t)gamma * 4, hipMemcpyDeviceToHost, st));
+    HIPCHK(hipMemcpyAsync(hres + gamma, m->lm_idx, (size_t)n * 4, hipMemcpyDeviceToHost, st));
+    return KNAPSPEC_OK;
   };
 
   // ---- run: like a solve, replay a captured graph when the configuration (layer set, gamma,
