@@ -1,6 +1,7 @@
 """GPU knapspec_solve with r-token windows and the LM-head acceptance estimate vs the oracle.
 
-* Windows r = 2..8 on the float32 tiny decoder and r = 4 on a bf16 MFMA-path decoder:
+* Windows r = 2..8 on the float32 tiny decoder, r = 4 on a bf16 MFMA-path decoder and r = 5
+  with the LM-head estimate on the full Qwen3-1.7B preset:
   rules P1-P4 (tests/parity.py) with the oracle's window DP (causal block attention over the
   cache, flattened r x d cosine).
 * A model loaded for windows up to 4 solving r = 1 matches the single-token oracle.
@@ -110,3 +111,9 @@ def test_bf16_window_lm_head_alpha():
     wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=3, d_model=1024, d_ff=2048,
                 name="qwen_like_lm")
     run_window(wl, 4, ctx=700, n_budgets=48, lm_vocab=4096)
+
+
+def test_qwen3_1p7b_full_preset_window_lm_head():
+    # the full Qwen3-1.7B preset (28 layers, n = 4096, 128 budgets) with r = 5 token states
+    # (one from each of the last m = 5 steps) and the LM-head estimate over 32768 rows
+    run_window(WORKLOADS["qwen3_1p7b_4k"], 5, ctx=4096, lm_vocab=32768)
