@@ -103,3 +103,13 @@ def test_repeated_calls_replay_the_captured_graph():
         assert r["accepted"] == orc.accepted
     print(f"\n  draft us per call: {[round(r['draft_us']) for r in runs]}", flush=True)
     prob.close()
+
+
+def test_qwen3_1p7b_full_preset_draft_verify():
+    # the full Qwen3-1.7B preset (28 layers, n = 4096) with its DP pick, gamma = 8 (the largest
+    # draft length of the preset's grid) and an LM head of 32768 rows
+    out = run_draft(WORKLOADS["qwen3_1p7b_4k"], 4096, 8, 32768, _masks)
+    assert any(k > 0 for _, _, _, k in out)
+    full = [o for o in out if o[0] == "full"][0]
+    # every item executed: the draft is the target; tokens compared up to the first near-tie
+    assert full[1]["accepted"] >= full[3]
