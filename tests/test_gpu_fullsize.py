@@ -6,7 +6,11 @@ The oracle cannot redo a whole Llama-3-8B-shape DP in test time, so each case ch
     per-cell decisions walk back to the returned masks; t_draft is the sum of the executed
     items' latencies; the (b, gamma) pick is the TPT argmax of the returned cosines;
   * the oracle's DP on a prefix of the items (P1 on those cells, tie-aware);
-  * the oracle's forward of a sample of returned masks (P2: cosine within the band).
+  * the oracle's forward of a sample of returned masks (P2: cosine within the band);
+  * for the r-token window with the LM-head estimate and for the beam variant (the bench's
+    --window 5 --lm-vocab 32768 and --beam 4 lines): the same properties (the pick on the
+    returned alphas), P2 on sampled masks, and for the window the greedy tokens of the sampled
+    budgets and of the full model against the oracle's (tokens inside the logit band excused).
 """
 import math
 import time
@@ -34,7 +38,7 @@ def reachable(w, B):
     return r
 
 
-def check_structure(res, q, t, B, gamma, n_items, t_target):
+def check_structure(res, q, t, B, gamma, n_items, t_target, decisions=True, alpha=None):
     w = res.item_weight[q].astype(np.int64)
     valid = res.valid[q].astype(bool)
     assert np.array_equal(valid, reachable(w, B))
@@ -45,8 +49,8 @@ def check_structure(res, q, t, B, gamma, n_items, t_target):
             assert res.t_draft[q][b] == pytest.approx(float(np.sum(t[bits[b]])), rel=1e-12)
         else:
             assert not bits[b].any()
-    dec = res.decisions[q]
-    for b0 in np.nonzero(valid)[0]:
+    dec = res.decisions[q] if decisions else None
+    for b0 in (np.nonzero(valid)[0] if decisions else []):
         b, got = int(b0), np.zeros(n_items, dtype=bool)
         for i in range(n_items - 1, -1, -1):
             assert dec[i][b] in (0, 1)
@@ -56,7 +60,8 @@ def check_structure(res, q, t, B, gamma, n_items, t_target):
         assert b == 0 and np.array_equal(got, bits[b0])
     c = res.cos[q]
     assert np.all(c[valid] <= 1.0 + 1e-6) and np.all(np.isnan(c[~valid]))
-    alpha = np.clip(np.nan_to_num(c.astype(np.float64), nan=0.0), 0.0, 1.0)
+    if alpha is None:
+        alpha = np.clip(np.nan_to_num(c.astype(np.float64), nan=0.0), 0.0, 1.0)
     pick = ko.tpt_select(alpha, res.t_draft[q], valid, t_target, gamma[0], gamma[1])
     assert (pick[0], pick[1]) == (int(res.best_budget[q]), int(res.best_gamma[q]))
 
@@ -145,4 +150,85 @@ def test_llama3_8b_x16_resolve_schedule():
                                         ctx=ctxs[q], x0=prob.resolve_x0[q][r])
         print(f"  resolve {r}: picks {[(int(b), int(g)) for b, g in zip(res.best_budget, res.best_gamma)]}",
               flush=True)
+    prob.close()
+
+
+def sample_budgets(res, q, n_sample, rng):
+    valid = np.nonzero(res.valid[q])[0]
+    picks = set(rng.choice(valid, size=min(n_sample, len(valid)), replace=False).tolist())
+    picks |= {int(valid[0]), int(valid[-1])}
+    if res.best_budget[q] >= 0:
+        picks.add(int(res.best_budget[q]))
+    return sorted(picks)
+
+
+@pytest.mark.timeout(900)
+def test_llama3_8b_32k_full_window5_lm_head():
+    from tests.parity import forward_states
+    from workloads.device import DeviceProblem
+
+    wl = WORKLOADS["llama3_8b_32k"]
+    s = wl.shape
+    r, vocab, band = 5, 32768, 0.05
+    print(f"\n[case] {wl.name} full size, window r={r}, LM head {vocab}", flush=True)
+    prob = DeviceProblem(wl, 0, keep_host=True, window=r, lm_vocab=vocab)
+    res = prob.solve(flags=3 | prob.ks.KNAPSPEC_ALPHA_LM_HEAD)
+    n_items, ctx, x0 = 2 * s.n_layers, prob.ctxs[0], prob.host_x0[0]
+    lat = wl.latency
+    t = ko.item_latencies(s.n_layers, ctx, lat.attn_base, lat.attn_per_token, lat.mlp)
+    w = ko.item_weights(t, wl.n_budgets)
+    assert np.array_equal(res.item_weight[0], w.astype(np.int32))
+    check_structure(res, 0, t, wl.n_budgets, wl.gamma, n_items, float(np.sum(t)),
+                    alpha=res.alpha[0].astype(np.float64))
+    items = ko.DecoderItems(decoder_shape(wl), prob.host_layers, prob.host_kv[0], ctx)
+    picks = sample_budgets(res, 0, 5, np.random.default_rng(2))
+    bits = ko.unpack_masks(res.masks[0], n_items)[picks]
+    t0 = time.time()
+    st, ref = forward_states(items, n_items, x0, bits)
+    cos = np.array([ko.cos_rows(st[k][None], ref)[0] for k in range(len(picks))])
+    err = np.abs(cos - res.cos[0][picks].astype(np.float64))
+    print(f"  P2 on budgets {picks}: max err {err.max():.2e} ({time.time() - t0:.1f}s)", flush=True)
+    assert err.max() <= BETA[s.dtype]
+    # greedy tokens of the sampled budgets and of the full model
+    tok_g = res.tokens(0)
+    tok_o, mar_o = ko.greedy_tokens(st, prob.host_lm, s.rms_eps)
+    tref, mref = ko.greedy_tokens(np.asarray(ref).reshape(r, -1), prob.host_lm, s.rms_eps)
+    B = wl.n_budgets
+    clean_ref = mref >= band
+    assert np.all((tok_g[B] == tref) | ~clean_ref)
+    mism = excused = 0
+    for k, b in enumerate(picks):
+        clean = (mar_o[k] >= band) & clean_ref
+        excused += int(np.sum(~clean))
+        mism += int(np.sum((tok_g[b] != tok_o[k]) & clean))
+        assert abs(float(res.alpha[0][b]) - float(np.sum(tok_g[b] == tok_g[B])) / r) <= 1e-6
+    print(f"  tokens: {len(picks) * r} compared, {excused} excused, {mism} mismatched", flush=True)
+    assert mism == 0
+    prob.close()
+
+
+@pytest.mark.timeout(900)
+def test_llama3_8b_32k_full_beam4():
+    from workloads.device import DeviceProblem
+
+    wl = WORKLOADS["llama3_8b_32k"]
+    s = wl.shape
+    print(f"\n[case] {wl.name} full size, beam 4", flush=True)
+    prob = DeviceProblem(wl, 0, keep_host=True, max_beam=4)
+    res = prob.solve(beam=4)
+    n_items, ctx, x0 = 2 * s.n_layers, prob.ctxs[0], prob.host_x0[0]
+    lat = wl.latency
+    t = ko.item_latencies(s.n_layers, ctx, lat.attn_base, lat.attn_per_token, lat.mlp)
+    w = ko.item_weights(t, wl.n_budgets)
+    assert np.array_equal(res.item_weight[0], w.astype(np.int32))
+    check_structure(res, 0, t, wl.n_budgets, wl.gamma, n_items, float(np.sum(t)),
+                    decisions=False)
+    items = ko.DecoderItems(decoder_shape(wl), prob.host_layers, prob.host_kv[0], ctx)
+    picks = sample_budgets(res, 0, 6, np.random.default_rng(3))
+    bits = ko.unpack_masks(res.masks[0], n_items)[picks]
+    t0 = time.time()
+    ev = ko.eval_subsets(items, n_items, x0, bits)
+    err = np.abs(ev - res.cos[0][picks].astype(np.float64))
+    print(f"  P2 on budgets {picks}: max err {err.max():.2e} ({time.time() - t0:.1f}s)", flush=True)
+    assert err.max() <= BETA[s.dtype]
     prob.close()
