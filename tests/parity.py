@@ -59,7 +59,10 @@ def clean_cells(oracle: ko.SolveResult, beta: float) -> np.ndarray:
 
 
 def compare(oracle: ko.SolveResult, gpu_res, seq: int, beta: float, apply_item, x0,
-            gamma, n_items: int) -> ParityReport:
+            gamma, n_items: int, p2_cos=None) -> ParityReport:
+    """``p2_cos`` (optional, float64 [B]): the oracle's cosine of every valid GPU budget's
+    mask, already computed (e.g. by LockstepSubsets alongside the DP); otherwise P2 runs
+    eval_subsets here."""
     dp = oracle.dp
     B = dp.valid.shape[0]
     assert np.array_equal(gpu_res.item_weight[seq], oracle.w.astype(np.int32)), \
@@ -79,7 +82,8 @@ def compare(oracle: ko.SolveResult, gpu_res, seq: int, beta: float, apply_item, 
     p2 = 0.0
     ev = np.full(B, np.nan)
     if len(vb):
-        ev[vb] = ko.eval_subsets(apply_item, n_items, x0, gbits[vb])
+        ev[vb] = (np.asarray(p2_cos)[vb] if p2_cos is not None
+                  else ko.eval_subsets(apply_item, n_items, x0, gbits[vb]))
         p2 = float(np.max(np.abs(ev[vb] - gpu_res.cos[seq][vb].astype(np.float64))))
     same_mask = valid_g & dp.valid & np.all(gbits == dp.bits, axis=1)
     dcos = 0.0

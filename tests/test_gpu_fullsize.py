@@ -1,16 +1,16 @@
 """Full-size presets on the GPU, in the launch configuration bench.py times.
 
-The oracle cannot redo a whole Llama-3-8B-shape DP in test time, so each case checks
-  * properties that hold at any size: item weights equal the oracle's; valid budgets are
-    exactly the reachable weight sums; every valid mask's weights sum to its budget; the
-    per-cell decisions walk back to the returned masks; t_draft is the sum of the executed
-    items' latencies; the (b, gamma) pick is the TPT argmax of the returned cosines;
-  * the oracle's DP on a prefix of the items (P1 on those cells, tie-aware);
-  * the oracle's forward of a sample of returned masks (P2: cosine within the band);
-  * for the r-token window with the LM-head estimate and for the beam variant (the bench's
-    --window 5 --lm-vocab 32768 and --beam 4 lines): the same properties (the pick on the
-    returned alphas), P2 on sampled masks, and for the window the greedy tokens of the sampled
-    budgets and of the full model against the oracle's (tokens inside the logit band excused).
+Llama-3-8B 32K (the headline) and the 16-sequence re-solve schedule are compared with the
+oracle's WHOLE DP (tests/parity.py: P1 on every cell, P2 on every valid budget's mask, P3 on
+the valid sets, P4 on the (b, gamma) pick), the oracle's forward of the GPU's masks riding
+along the DP's item calls (helpers.LockstepSubsets).  Every case also checks properties that
+hold at any size: item weights equal the oracle's; valid budgets are exactly the reachable
+weight sums; every valid mask's weights sum to its budget; the per-cell decisions walk back to
+the returned masks; t_draft is the sum of the executed items' latencies; the (b, gamma) pick
+is the TPT argmax of the returned cosines.  The bench's variant lines at full size (r = 5
+windows with the LM-head estimate, and beam 4) are checked on those properties, P2 on sampled
+masks and, for the window, the greedy tokens of the sampled budgets and of the full model
+against the oracle's (tokens inside the logit band excused).
 """
 import math
 import time
@@ -20,7 +20,6 @@ import pytest
 
 from oracle import knapspec_oracle as ko
 from tests.helpers import decoder_shape
-from tests.parity import clean_cells
 from workloads import WORKLOADS
 
 pytestmark = pytest.mark.gpu
@@ -66,57 +65,51 @@ def check_structure(res, q, t, B, gamma, n_items, t_target, decisions=True, alph
     assert (pick[0], pick[1]) == (int(res.best_budget[q]), int(res.best_gamma[q]))
 
 
-def check_prefix_and_sample(prob, res, q, wl, prefix_layers, n_sample, rng, ctx=None, x0=None):
+def full_parity(layers, prob, res, q, wl, ctx, x0, label=""):
+    """The oracle's whole solve for sequence q against the GPU's (P1-P4 on every cell)."""
+    from tests.helpers import LockstepSubsets
+    from tests.parity import compare
+
     s = wl.shape
     n_items = 2 * s.n_layers
-    beta = BETA[s.dtype]
-    lat = wl.latency
-    ctx = prob.ctxs[q] if ctx is None else ctx
-    x0 = prob.host_x0[q] if x0 is None else x0
-    t = ko.item_latencies(s.n_layers, ctx, lat.attn_base, lat.attn_per_token, lat.mlp)
-    w = ko.item_weights(t, wl.n_budgets)
-    assert np.array_equal(res.item_weight[q], w.astype(np.int32))
-    check_structure(res, q, t, wl.n_budgets, wl.gamma, n_items, float(np.sum(t)))
-    items = ko.DecoderItems(decoder_shape(wl), prob.host_layers, prob.host_kv[q], ctx)
-    # oracle on the first items: decisions on clean cells must agree
-    k = 2 * prefix_layers
-    t0 = time.time()
-    pre = ko.knapsack_dp(items, k, w[:k], x0, wl.n_budgets)
-    fake = ko.SolveResult(dp=pre, t=t[:k], w=w[:k], masks=None, t_draft=None, t_target=0,
-                          best_budget=-1, best_gamma=-1, best_tpt=0)
-    clean = clean_cells(fake, beta)
-    mism = int(np.sum((res.decisions[q][:k] != pre.decisions) & clean))
-    print(f"  seq {q} ctx {ctx}: prefix {k} items in {time.time() - t0:.1f}s, clean {clean.sum()}/"
-          f"{clean.size}, clean mismatches {mism}", flush=True)
-    assert mism == 0
-    # oracle forward of sampled returned masks
+    lat = {"attn_base": wl.latency.attn_base, "attn_per_token": wl.latency.attn_per_token,
+           "mlp": wl.latency.mlp, "fixed": wl.latency.fixed}
+    items = ko.DecoderItems(decoder_shape(wl), layers, prob.host_kv[q], ctx)
     valid = np.nonzero(res.valid[q])[0]
-    picks = set(rng.choice(valid, size=min(n_sample, len(valid)), replace=False).tolist())
-    picks |= {int(valid[0]), int(valid[-1])}
-    if res.best_budget[q] >= 0:
-        picks.add(int(res.best_budget[q]))
-    picks = sorted(picks)
-    bits = ko.unpack_masks(res.masks[q], n_items)[picks]
+    bits = ko.unpack_masks(res.masks[q], n_items)[valid]
+    lock = LockstepSubsets(items, x0, bits)
     t0 = time.time()
-    ev = ko.eval_subsets(items, n_items, x0, bits)
-    err = np.abs(ev - res.cos[q][picks].astype(np.float64))
-    print(f"  seq {q}: P2 on budgets {picks}: max err {err.max():.2e} ({time.time() - t0:.1f}s)",
-          flush=True)
-    assert err.max() <= beta
+    orc = ko.solve(decoder_shape(wl), None, None, x0, ctx, lat, wl.n_budgets, wl.gamma,
+                   apply_item=lock)
+    p2 = np.full(wl.n_budgets, np.nan)
+    p2[valid] = lock.cos(orc.dp.ref)
+    rep = compare(orc, res, q, BETA[s.dtype], None, x0, wl.gamma, n_items, p2_cos=p2)
+    print(f"  {label}seq {q} ctx {ctx}: oracle DP + P2 in {time.time() - t0:.1f}s; "
+          f"{rep.line()}; pick gpu ({int(res.best_budget[q])}, {int(res.best_gamma[q])}) "
+          f"oracle ({orc.best_budget}, {orc.best_gamma})", flush=True)
+    assert rep.mismatched_clean == 0
+    assert rep.p2_max_err <= BETA[s.dtype]
+    assert rep.p3_bad == 0
+    assert rep.p4_ok
+    return orc, rep
 
 
 @pytest.mark.timeout(900)
 def test_llama3_8b_32k_full():
+    from tests.helpers import WidenedLayers
     from workloads.device import DeviceProblem
 
     wl = WORKLOADS["llama3_8b_32k"]
-    print(f"\n[case] {wl.name} full size", flush=True)
+    print(f"\n[case] {wl.name} full size, whole-DP parity", flush=True)
     prob = DeviceProblem(wl, 0, keep_host=True)
     res = prob.solve(flags=3)
     res2 = prob.solve(flags=3)
     assert np.array_equal(res.masks, res2.masks) and np.array_equal(res.decisions, res2.decisions)
-    check_prefix_and_sample(prob, res, 0, wl, prefix_layers=3, n_sample=6,
-                            rng=np.random.default_rng(0))
+    s, lat = wl.shape, wl.latency
+    t = ko.item_latencies(s.n_layers, prob.ctxs[0], lat.attn_base, lat.attn_per_token, lat.mlp)
+    check_structure(res, 0, t, wl.n_budgets, wl.gamma, 2 * s.n_layers, float(np.sum(t)))
+    full_parity(WidenedLayers(prob.host_layers), prob, res, 0, wl, prob.ctxs[0],
+                prob.host_x0[0])
     prob.close()
 
 
@@ -124,18 +117,19 @@ def test_llama3_8b_32k_full():
 def test_llama3_8b_x16_resolve_schedule():
     """16 sequences, contexts lognormal in [2K, 32K], re-solved every 256 tokens (8 times),
     all sequences batched into each solve.  Every sequence of every re-solve is checked for
-    the structural properties; two sequences at the first and last re-solve against the
-    oracle (DP prefix and sampled masks)."""
+    the structural properties; every sequence at the first and the last re-solve against
+    the oracle's whole DP."""
+    from tests.helpers import WidenedLayers
     from workloads.device import DeviceProblem
 
     wl = WORKLOADS["llama3_8b_x16"]
     print(f"\n[case] {wl.name}", flush=True)
     prob = DeviceProblem(wl, 0, keep_host=True)
     print(f"  contexts {prob.ctxs}", flush=True)
+    layers = WidenedLayers(prob.host_layers, keep_all=True)
     s = wl.shape
     n_items = 2 * s.n_layers
     lat = wl.latency
-    rng = np.random.default_rng(1)
     for r in range(wl.resolves):
         res = prob.solve(flags=3, resolve=r)
         ctxs = prob.resolve_ctxs(r)
@@ -144,12 +138,12 @@ def test_llama3_8b_x16_resolve_schedule():
             w = ko.item_weights(t, wl.n_budgets)
             assert np.array_equal(res.item_weight[q], w.astype(np.int32))
             check_structure(res, q, t, wl.n_budgets, wl.gamma, n_items, float(np.sum(t)))
-        if r in (0, wl.resolves - 1):
-            for q in (int(np.argmin(ctxs)), int(np.argmax(ctxs))):
-                check_prefix_and_sample(prob, res, q, wl, prefix_layers=2, n_sample=3, rng=rng,
-                                        ctx=ctxs[q], x0=prob.resolve_x0[q][r])
         print(f"  resolve {r}: picks {[(int(b), int(g)) for b, g in zip(res.best_budget, res.best_gamma)]}",
               flush=True)
+        if r in (0, wl.resolves - 1):
+            for q in range(len(ctxs)):
+                full_parity(layers, prob, res, q, wl, ctxs[q], prob.resolve_x0[q][r],
+                            label=f"resolve {r} ")
     prob.close()
 
 

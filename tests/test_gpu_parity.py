@@ -59,6 +59,24 @@ def test_tiny_f32_full_preset():
     assert rep.same_pick
 
 
+def test_tiny_f32_fixed_latency_interior_pick():
+    # A per-pass latency `fixed` equal to one MLP item's makes the empty draft cost something,
+    # so the TPT pick moves off the (b = 0, gamma = gamma_max) corner into the grid (the
+    # oracle picks b = 5, gamma = 1 on seed 0); the float32 path must reproduce it exactly.
+    from workloads.configs import LatencyModel
+
+    wl = scaled(WORKLOADS["tiny"], latency=LatencyModel(1.0, 0.01, 2.0, 2.0),
+                name="tiny_fixed2")
+    res, reps = run_case(wl)
+    orc, rep = reps[0]
+    assert rep.excused == 0 and rep.same_pick
+    assert np.array_equal(res.masks[0], orc.masks)
+    assert 0 < orc.best_budget < wl.n_budgets - 1
+    assert (int(res.best_budget[0]), int(res.best_gamma[0])) == (orc.best_budget, orc.best_gamma)
+    assert np.allclose(res.t_draft[0][orc.dp.valid], orc.t_draft[orc.dp.valid], rtol=0, atol=1e-12)
+    assert float(res.best_tpt[0]) == pytest.approx(orc.best_tpt, rel=1e-6)
+
+
 @pytest.mark.parametrize("ctx", [0, 1, 77, 300])
 def test_tiny_f32_context_edges(ctx):
     run_case(WORKLOADS["tiny"], ctxs=[ctx])
