@@ -212,6 +212,13 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_init(const InitArgs& a, hipStream_t s);
 
+// Static device scratch (scratch.hip): STATIC_SCRATCH_BYTES in one file-scope __device__ array
+// per GPU.  resolve_static_scratch takes its device address once per device (call with that
+// device current); static_scratch returns it (nullptr until resolved).
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t resolve_static_scratch(int device);
+void* static_scratch(int device);
+
 // rows of Q per attention workgroup for the given activation type / head size
 int attention_qblock(int act, int dh);
 // attention workgroups resident per compute unit (LDS / register limited)

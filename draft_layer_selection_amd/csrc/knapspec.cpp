@@ -162,9 +162,12 @@ struct knapspec_model {
   size_t part_slots = 0;  // attention partial results: (split, row, query head) slots
   int n_cus = 0;
 
-  // device workspace
+  // device workspace: one allocation carved at these byte offsets (point_workspace)
   char* ws = nullptr;
   size_t ws_bytes = 0;
+  struct {
+    size_t state, valid, masks, xa, q, ks, vs, o, h, P, E, Op, Mp, Lp, dec, mar, cos, maps;
+  } wo{};
   float* state[2]{};
   uint8_t* valid[2]{};
   uint64_t* masks[2]{};
@@ -376,6 +379,39 @@ KS_API int knapspec_tpt_select(const float* alpha, const double* t_draft, const 
 
 KS_API void knapspec_free_model(knapspec_model* m) { delete m; }
 
+namespace {
+
+// Points every per-solve device buffer of the model into the workspace at `ws` (the model's
+// own allocation, or the static scratch for knapspec_solve_static).
+void point_workspace(knapspec_model* m, char* ws) {
+  const auto& wo = m->wo;
+  const size_t S = m->desc.max_seqs, Bm = m->desc.max_budgets, D = m->desc.d_model;
+  const size_t Kb = m->kmax, Wm = m->wmax;
+  m->state[0] = (float*)(ws + wo.state);
+  m->state[1] = m->state[0] + S * (Bm + 1) * Kb * Wm * D;
+  m->valid[0] = (uint8_t*)(ws + wo.valid);
+  m->valid[1] = m->valid[0] + S * Bm * Kb;
+  m->masks[0] = (uint64_t*)(ws + wo.masks);
+  m->masks[1] = m->masks[0] + S * Bm * Kb * m->mw;
+  m->xa = ws + wo.xa;
+  m->q = ws + wo.q;
+  m->kself = (float*)(ws + wo.ks);
+  m->vself = (float*)(ws + wo.vs);
+  m->o = ws + wo.o;
+  m->h = ws + wo.h;
+  m->P = (float*)(ws + wo.P);
+  m->E = (float*)(ws + wo.E);
+  m->Opart = (float*)(ws + wo.Op);
+  m->Mpart = (float*)(ws + wo.Mp);
+  m->Lpart = (float*)(ws + wo.Lp);
+  m->decisions = (uint8_t*)(ws + wo.dec);
+  m->margins = (float*)(ws + wo.mar);
+  m->cos = (float*)(ws + wo.cos);
+  m->maps = ws + wo.maps;
+}
+
+}  // namespace
+
 KS_API int knapspec_load_model(const knapspec_model_desc* desc,
                                const knapspec_layer_weights* layers, void* hip_stream,
                                knapspec_model** out) {
@@ -462,29 +498,30 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
   m->p_floats = std::max<size_t>(PSPLIT_MAX * std::min<size_t>(R, 256), R) * nmax;
 
   Carver c;
-  const size_t o_state = c.take(2 * S * (Bm + 1) * Kb * Wm * D * 4);
-  const size_t o_valid = c.take(2 * S * Bm * Kb);
-  const size_t o_masks = c.take(2 * S * Bm * Kb * m->mw * 8);
-  const size_t o_xa = c.take(R * D * m->elem);
-  const size_t o_q = c.take(R * m->qdim * m->elem);
-  const size_t o_ks = c.take(R * m->kvdim * 4);
-  const size_t o_vs = c.take(R * m->kvdim * 4);
-  const size_t o_o = c.take(R * m->qdim * m->elem);
-  const size_t o_h = c.take(R * d.d_ff * m->elem);
-  const size_t o_P = c.take(m->p_floats * 4);
-  const size_t o_E = c.take(R * D * 4);
+  auto& wo = m->wo;
+  wo.state = c.take(2 * S * (Bm + 1) * Kb * Wm * D * 4);
+  wo.valid = c.take(2 * S * Bm * Kb);
+  wo.masks = c.take(2 * S * Bm * Kb * m->mw * 8);
+  wo.xa = c.take(R * D * m->elem);
+  wo.q = c.take(R * m->qdim * m->elem);
+  wo.ks = c.take(R * m->kvdim * 4);
+  wo.vs = c.take(R * m->kvdim * 4);
+  wo.o = c.take(R * m->qdim * m->elem);
+  wo.h = c.take(R * d.d_ff * m->elem);
+  wo.P = c.take(m->p_floats * 4);
+  wo.E = c.take(R * D * 4);
   m->part_slots = (size_t)d.n_q_heads * std::max<size_t>(ASPLIT_MAX * std::min<size_t>(R, 512), R);
-  const size_t o_Op = c.take(m->part_slots * d.head_dim * 4);
-  const size_t o_Mp = c.take(m->part_slots * 4);
-  const size_t o_Lp = c.take(m->part_slots * 4);
-  const size_t o_dec = c.take(S * m->L2 * Bm);
-  const size_t o_mar = c.take(S * m->L2 * Bm * 4);
-  const size_t o_cos = c.take(S * Bm * 4);
+  wo.Op = c.take(m->part_slots * d.head_dim * 4);
+  wo.Mp = c.take(m->part_slots * 4);
+  wo.Lp = c.take(m->part_slots * 4);
+  wo.dec = c.take(S * m->L2 * Bm);
+  wo.mar = c.take(S * m->L2 * Bm * 4);
+  wo.cos = c.take(S * Bm * 4);
   // row maps and launch tables, rebuilt on the host each solve and uploaded once
   const int G = d.n_q_heads / d.n_kv_heads;
   m->maps_bytes = map_layout(m->L2, d.n_layers, S, Bm, R, d.n_kv_heads, G, d.head_dim,
                              ASPLIT_MAX, Wm, Kb).total;
-  const size_t o_maps = c.take(m->maps_bytes);
+  wo.maps = c.take(m->maps_bytes);
   m->ws_bytes = c.off;
 
   if (hipMalloc((void**)&m->ws, m->ws_bytes) != hipSuccess) {
@@ -510,28 +547,13 @@ KS_API int knapspec_load_model(const knapspec_model_desc* desc,
     delete m;
     return fail(KNAPSPEC_EHIP, "stream/event creation failed");
   }
-  char* ws = m->ws;
-  m->state[0] = (float*)(ws + o_state);
-  m->state[1] = m->state[0] + S * (Bm + 1) * Kb * Wm * D;
-  m->valid[0] = (uint8_t*)(ws + o_valid);
-  m->valid[1] = m->valid[0] + S * Bm * Kb;
-  m->masks[0] = (uint64_t*)(ws + o_masks);
-  m->masks[1] = m->masks[0] + S * Bm * Kb * m->mw;
-  m->xa = ws + o_xa;
-  m->q = ws + o_q;
-  m->kself = (float*)(ws + o_ks);
-  m->vself = (float*)(ws + o_vs);
-  m->o = ws + o_o;
-  m->h = ws + o_h;
-  m->P = (float*)(ws + o_P);
-  m->E = (float*)(ws + o_E);
-  m->Opart = (float*)(ws + o_Op);
-  m->Mpart = (float*)(ws + o_Mp);
-  m->Lpart = (float*)(ws + o_Lp);
-  m->decisions = (uint8_t*)(ws + o_dec);
-  m->margins = (float*)(ws + o_mar);
-  m->cos = (float*)(ws + o_cos);
-  m->maps = ws + o_maps;
+  point_workspace(m, m->ws);
+  // set-up of the static device scratch of knapspec_solve_static (once per device)
+  if (ks::resolve_static_scratch(m->device) != hipSuccess) {
+    (void)hipGetLastError();
+    delete m;
+    return fail(KNAPSPEC_EHIP, "static scratch address lookup failed");
+  }
   *out = m;
   return KNAPSPEC_OK;
 }
@@ -648,8 +670,12 @@ struct SeqPlan {
 
 }  // namespace
 
-KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
-                          knapspec_result* res) {
+namespace {
+
+// One solve.  static_ws: the model's buffers already point into the static scratch; launch
+// eagerly (no graph capture or instantiation, no profiling events), so nothing is allocated.
+int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_result* res,
+               bool static_ws) {
   if (!m || !args || !res) return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
   const knapspec_model_desc& d = m->desc;
   if (!m->have_latency) return fail(KNAPSPEC_EINVAL, "latency model not set");
@@ -1146,7 +1172,7 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
   //      (always when profiling or when KNAPSPEC_GRAPHS=0).
   hipStream_t caller = (hipStream_t)args->hip_stream;
   const char* genv = std::getenv("KNAPSPEC_GRAPHS");
-  const bool graphs = !m->profiling && !(genv && genv[0] == '0') && m->own_stream;
+  const bool graphs = !static_ws && !m->profiling && !(genv && genv[0] == '0') && m->own_stream;
   if (!graphs) {
     int rc = enqueue(caller);
     if (rc) return rc;
@@ -1263,6 +1289,34 @@ KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
     }
   }
   return KNAPSPEC_OK;
+}
+
+}  // namespace
+
+KS_API int knapspec_solve(knapspec_model* m, const knapspec_solve_args* args,
+                          knapspec_result* res) {
+  return solve_impl(m, args, res, false);
+}
+
+KS_API int knapspec_solve_static(knapspec_model* m, const knapspec_solve_args* args,
+                                 knapspec_result* res) {
+  if (!m) return fail(KNAPSPEC_EINVAL, "model is NULL");
+  if (m->ws_bytes > ks::STATIC_SCRATCH_BYTES)
+    return fail(KNAPSPEC_EINVAL,
+                "the model's per-solve buffers need %zu bytes; the static scratch holds %zu "
+                "(load the model with smaller max_budgets / max_seqs / max_window / max_beam)",
+                m->ws_bytes, (size_t)ks::STATIC_SCRATCH_BYTES);
+  if (m->profiling)
+    return fail(KNAPSPEC_EINVAL, "profiling is enabled (it records events): disable it first");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != m->device)
+    return fail(KNAPSPEC_EINVAL, "current HIP device differs from the model's device");
+  char* sp = (char*)ks::static_scratch(dev);
+  if (!sp) return fail(KNAPSPEC_EHIP, "static scratch not resolved on device %d", dev);
+  point_workspace(m, sp);
+  const int rc = solve_impl(m, args, res, true);
+  point_workspace(m, m->ws);
+  return rc;
 }
 
 // ------------------------------------------------------------------------------------------

@@ -81,6 +81,8 @@ SIGNATURES = {
     "knapspec_set_latency_model": (C.c_int, [C.c_void_p, C.POINTER(knapspec_latency_model)]),
     "knapspec_solve": (C.c_int, [C.c_void_p, C.POINTER(knapspec_solve_args),
                                  C.POINTER(knapspec_result)]),
+    "knapspec_solve_static": (C.c_int, [C.c_void_p, C.POINTER(knapspec_solve_args),
+                                        C.POINTER(knapspec_result)]),
     "knapspec_tpt_select": (C.c_int, [C.POINTER(C.c_float), C.POINTER(C.c_double),
                                       C.POINTER(C.c_uint8), C.c_int32, C.c_double, C.c_int32,
                                       C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
@@ -121,6 +123,7 @@ for _name, (_res, _args) in SIGNATURES.items():
 knapspec_load_model = lib.knapspec_load_model
 knapspec_set_latency_model = lib.knapspec_set_latency_model
 knapspec_solve = lib.knapspec_solve
+knapspec_solve_static = lib.knapspec_solve_static
 knapspec_tpt_select = lib.knapspec_tpt_select
 knapspec_item_weights = lib.knapspec_item_weights
 knapspec_set_profiling = lib.knapspec_set_profiling
@@ -271,10 +274,12 @@ class Model:
 
     def solve(self, seqs: List[dict], n_budgets: int, gamma, tau: float = -math.inf,
               max_skip_weight: int = -1, flags: int = 0, stream=None,
-              result: Optional[Result] = None, beam: int = 1) -> Result:
+              result: Optional[Result] = None, beam: int = 1,
+              static_scratch: bool = False) -> Result:
         """seqs: dicts with ctx (int), k_cache / v_cache (lists of device tensors per layer,
         [hkv][capacity][dh]), x0 (device float32 [window][d] or [d]) and optionally window
-        (int, default 1)."""
+        (int, default 1).  static_scratch: call knapspec_solve_static (per-solve device
+        buffers in the library's static scratch; allocates nothing)."""
         torch = self._torch
         S = len(seqs)
         carr, keep = self._seq_array(seqs)
@@ -285,7 +290,9 @@ class Model:
         res = result if result is not None else Result(
             S, n_budgets, 2 * self.n_layers, self.mw, flags,
             windows=[int(sq.get("window", 1)) for sq in seqs])
-        _check(knapspec_solve(self.handle, C.byref(args), C.byref(res.struct)), "knapspec_solve")
+        fn, name = ((knapspec_solve_static, "knapspec_solve_static") if static_scratch
+                    else (knapspec_solve, "knapspec_solve"))
+        _check(fn(self.handle, C.byref(args), C.byref(res.struct)), name)
         return res
 
     def profile_items(self, seq: dict, ctx_lens, reps: int = 8, stream=None):

@@ -184,6 +184,24 @@ typedef struct {
 int knapspec_solve(knapspec_model* model, const knapspec_solve_args* args,
                    knapspec_result* result);
 
+/* knapspec_solve for callers that cannot allocate device memory (code under HIP graph capture
+ * of its surroundings, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and errors as knapspec_solve, and the same kernels; the difference is where the
+ * per-solve device buffers live (DP states, activation rows, GEMM and attention partial
+ * results, decisions, row maps): in one static device array of the library, 64 MiB per GPU,
+ * held from the first model load on that GPU until the process ends, instead of the model's
+ * workspace.  The call allocates nothing (no hipMalloc / hipFree, no events or graph
+ * instantiation; work is launched eagerly on hip_stream).
+ * Limits and errors: EINVAL when the model's per-solve buffers (sized at load from
+ * max_budgets, max_seqs, max_ctx, max_window, max_beam and the decoder shape) exceed 64 MiB --
+ * e.g. a 28-layer, d 2048 decoder loaded for 128 budgets fits, a Llama-3-8B shape for 256
+ * budgets does not -- or when profiling is enabled.  Nothing in the array needs to start at
+ * zero: every buffer a solve reads is written earlier in the same solve.  All calls on one GPU
+ * share the array: calls that overlap on one GPU (several threads, streams or models) race
+ * and must be serialised by the caller. */
+int knapspec_solve_static(knapspec_model* model, const knapspec_solve_args* args,
+                          knapspec_result* result);
+
 /* LM head for the acceptance estimate: w [vocab][d_model] in desc.dtype, a borrowed device
  * pointer kept alive and unchanged until the model is freed or the head replaced.  The
  * first call allocates the device buffers the estimate needs (a running argmax per row);
