@@ -164,6 +164,20 @@ def _pmc_per_kernel(path_dir, counter):
     return per
 
 
+def kernel_tag(name: str) -> str:
+    """Short file-name tag of a (demangled or mangled) kernel name: attention, gemm, select..."""
+    import re
+
+    if "attn" in name:
+        return "attention"
+    ids = re.findall(r"([A-Za-z_][A-Za-z0-9_]*?)(?:_kernel)?(?:<[^>]*>)?\(", name)
+    ids = [i for i in ids if i not in ("anonymous", "void")]
+    if ids:
+        return ids[0].split("_kernel")[0]
+    m = re.search(r"\d+([a-z_]+?)_kernel", name)  # mangled: ...14combine_kernelI...
+    return m.group(1) if m else "kernel"
+
+
 def summarize_profiles(args):
     """Write profiles/<kernel>_<workload>.md and profiles/traffic_<workload>.json from a
     kernel-trace --stats csv and four --pmc runs (bench FETCH_SIZE / WRITE_SIZE, copy
@@ -206,7 +220,7 @@ def summarize_profiles(args):
         wbs = f"{wb / 1e6:.2f}" if wb is not None else "-"
         md.append(f"| `{name[:90]}` | {calls} | {us:.1f} | {pct:.1f} | {fbs} | {wbs} |")
     dom = rows[0]
-    tag = "attention" if "attn" in dom[0] else dom[0].split("(")[0].split()[-1]
+    tag = kernel_tag(dom[0])
     out_md = os.path.join(PROFILES, f"{tag}_{args.workload}.md")
     open(out_md, "w").write("\n".join(md) + "\n")
     traffic = {"workload": args.workload, "kernel": dom[0], "source_sha": sha,
@@ -226,15 +240,22 @@ def ko_weights(wl, ctx):
     return [max(1, int(round(x / delta))) for x in t]
 
 
-def cpu_baseline(wl, prob, max_layers, log_fn, seconds=15.0):
-    """The oracle, untuned, on a bounded prefix of the same solve: the DP over the same inputs,
-    stopped at the first item boundary after ``seconds`` of wall time (or after ``max_layers``
-    layers).  The oracle runs unchanged; a wrapper around its item function only reads the
-    clock when the next item starts, so the timed prefix holds whole items (their forward and
-    their select).  The rate is scaled to whole solves by the fraction of the solve's FLOPs
-    the finished items hold."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _oracle_prefix(wl, prob, max_layers, seconds):
+    """One timed run of the unchanged oracle DP on a bounded prefix of the solve: stopped at
+    the first item boundary after ``seconds`` of wall time (or after ``max_layers`` layers).
+    A wrapper around the oracle's item function only reads the clock when the next item
+    starts, so the timed prefix holds whole items (their forward and their select).  Returns
+    (finished items, seconds, FLOP share of the solve those items hold)."""
     from oracle import knapspec_oracle as ko
 
     s = wl.shape
@@ -265,22 +286,52 @@ def cpu_baseline(wl, prob, max_layers, log_fn, seconds=15.0):
     except _Stop:
         pass
     n_items, dt = mark["done"], mark["t"]
-    # FLOP share of the finished prefix
     rows, _ = item_rows(list(w), wl.n_budgets)
     d, ff, dh, hq, hkv = s.d_model, s.d_ff, s.head_dim, s.n_q_heads, s.n_kv_heads
     qd, nqkv = hq * dh, (hq + 2 * hkv) * dh
+
     def item_flops(i):
         R = rows[i]
         if i % 2 == 0:
             return 2.0 * R * (nqkv * d + d * qd) + 4.0 * R * hq * prob.ctxs[0] * dh
         return 2.0 * R * 3 * ff * d
-    frac = sum(item_flops(i) for i in range(n_items)) / sum(item_flops(i) for i in range(2 * s.n_layers))
+    frac = (sum(item_flops(i) for i in range(n_items)) /
+            sum(item_flops(i) for i in range(2 * s.n_layers)))
+    return n_items, dt, frac
+
+
+def cpu_baseline(wl, prob, max_layers, log_fn, seconds=15.0, repeats=3, seconds_1t=8.0):
+    """The oracle, untuned, timed on the host cores over a bounded prefix of the same solve
+    (see _oracle_prefix), scaled to whole solves by the FLOP share of the finished items.
+    ``repeats`` runs with the BLAS pool on every core the process may use give the reported
+    value (their median); one more run with a single BLAS thread, capped at ``seconds_1t``,
+    is reported beside it."""
+    import statistics
+
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     threads = len(os.sched_getaffinity(0))
-    log_fn(f"[cpu] oracle {n_items} items in {dt:.2f}s = {frac:.3%} of one solve's FLOPs")
-    return {"value": frac / dt, "unit": "solves/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_items} of {2 * s.n_layers} items of one {wl.name} solve "
-                      f"(stopped at the first item boundary after {seconds:g} s), {dt:.1f}s; "
-                      f"scaled by its FLOP share {frac:.4f}"}
+    runs = []
+    with threadpool_limits(threads):
+        for k in range(repeats):
+            n_items, dt, frac = _oracle_prefix(wl, prob, max_layers, seconds)
+            runs.append((frac / dt, n_items, dt, frac))
+            log_fn(f"[cpu] oracle ({threads} threads) run {k}: {n_items} items in {dt:.2f}s = "
+                   f"{frac:.3%} of one solve's FLOPs")
+    with threadpool_limits(1):
+        n1, dt1, frac1 = _oracle_prefix(wl, prob, max_layers, seconds_1t)
+    log_fn(f"[cpu] oracle (1 thread): {n1} items in {dt1:.2f}s = {frac1:.3%} of one solve")
+    med = statistics.median(r[0] for r in runs)
+    blas = sorted({i.get("internal_api", "?") for i in threadpool_info()})
+    n_items = [r[1] for r in runs]
+    return {"value": med, "unit": "solves/s", "cores": threads, "kind": "oracle",
+            "sample": (f"median of {repeats} runs of the first items of one {wl.name} solve "
+                       f"({n_items} of {2 * wl.shape.n_layers} items; each stopped at the first "
+                       f"item boundary after {seconds:g} s), scaled by their FLOP share"),
+            "repeats": [round(r[0], 6) for r in runs],
+            "value_1_thread": frac1 / dt1 if dt1 > 0 else None,
+            "sample_1_thread": f"first {n1} items in {dt1:.1f}s (FLOP share {frac1:.4f})",
+            "cpu_model": cpu_model(), "blas": blas}
 
 
 def main():
@@ -292,7 +343,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=1000)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--summarize-profiles", action="store_true")
     ap.add_argument("--stats")
@@ -424,6 +476,8 @@ def main():
             roof["traffic"] = int(tr["fetch_bytes_per_launch"] + (tr["write_bytes_per_launch"] or 0))
             roof["traffic_algorithmic"] = int(bytes_per_launch)
     roof["kernel"] = dom
+    roof["timer"] = ("average launch duration from HIP events recorded around each launch on "
+                     "the solve stream (profiled pass)")
     log("[bench] kernel classes (avg us/launch, share of solve):")
     tot_ms = sum(v["total_ms"] for v in per_class.values())
     for k, v in sorted(per_class.items(), key=lambda kv: -kv[1]["total_ms"]):
@@ -433,11 +487,18 @@ def main():
     cpu = None
     if want_cpu:
         try:
-            cpu = cpu_baseline(wl, prob, args.cpu_layers, log, args.cpu_seconds)
+            cpu = cpu_baseline(wl, prob, args.cpu_layers, log, args.cpu_seconds,
+                               args.cpu_repeats)
         except Exception as e:  # the baseline is reported, never required for the GPU number
             log(f"[cpu] baseline failed: {e!r}")
+    headline = (wl.name == "llama3_8b_32k" and args.window == 1 and args.beam == 1
+                and not args.lm_vocab)
+    variant = "".join([f", window {args.window}" if args.window != 1 else "",
+                       f", beam {args.beam}" if args.beam != 1 else "",
+                       f", LM head {args.lm_vocab}" if args.lm_vocab else ""])
     line = {
-        "metric": METRIC,
+        "metric": METRIC if headline else
+                  f"KnapSpec DP solves/sec + achieved HBM GB/s, {wl.name}{variant}",
         "value": round(solves_per_s, 3),
         "unit": "solves/s",
         "n_gpus": 1,

@@ -106,12 +106,18 @@ def _small_problem():
 
 def test_cpu_baseline_whole_solve_and_early_stop():
     wl, prob = _small_problem()
-    full = bench.cpu_baseline(wl, prob, 1000, lambda *a: None, seconds=1e9)
+    full = bench.cpu_baseline(wl, prob, 1000, lambda *a: None, seconds=1e9, repeats=3,
+                              seconds_1t=1e9)
     assert full["kind"] == "oracle" and full["value"] > 0 and full["cores"] >= 1
-    assert "first 6 of 6 items" in full["sample"] and "share 1.0000" in full["sample"]
-    part = bench.cpu_baseline(wl, prob, 1000, lambda *a: None, seconds=0.0)
+    assert "[6, 6, 6] of 6 items" in full["sample"] and "median of 3" in full["sample"]
+    assert len(full["repeats"]) == 3 and sorted(full["repeats"])[1] == pytest.approx(full["value"], rel=1e-5)
+    assert full["value_1_thread"] > 0 and "first 6 items" in full["sample_1_thread"]
+    assert "(FLOP share 1.0000)" in full["sample_1_thread"]
+    assert full["cpu_model"] and full["blas"]
+    part = bench.cpu_baseline(wl, prob, 1000, lambda *a: None, seconds=0.0, repeats=1,
+                              seconds_1t=0.0)
     # stopped when item 1 starts: only item 0 (the first Attention item) was timed
-    assert "first 1 of 6 items" in part["sample"]
+    assert "[1] of 6 items" in part["sample"] and "first 1 items" in part["sample_1_thread"]
     assert part["value"] > 0
 
 
