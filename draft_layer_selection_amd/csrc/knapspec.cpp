@@ -736,8 +736,10 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     Rlm += (B + 1) * win[q];
   }
 
-  // ---- per-sequence weights and budget reachability (data independent when tau is off;
-  //      the kernels re-check validity on the device, so pruning only removes work).
+  // ---- per-sequence weights and budget reachability.  Rows are planned from reachability,
+  //      which does not depend on the data; tau and skip-cap pruning act on the device (the
+  //      select kernel invalidates cells), so a pruned budget keeps its rows in later items'
+  //      GEMMs and attention: pruning changes results, not the work done.
   std::vector<SeqPlan> plan(S);
   for (int q = 0; q < S; ++q) {
     SeqPlan& p = plan[q];
