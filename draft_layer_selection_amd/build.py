@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libknapspec.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["gemm.hip", "attention.hip", "select.hip", "scratch.hip", "knapspec.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "select.hip", "compact.hip", "scratch.hip", "knapspec.cpp"]
 ARCH = os.environ.get("KNAPSPEC_ARCH", "gfx950")
 
 

@@ -472,6 +472,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int G = a.hq / a.hkv;
   const int c = h / G;
   const AttnSeq S = a.seqs[a.row_seq[r]];
+  if (r - S.row_off >= S.M) return;  // a row past the live rows of a live-row plan
   const int e0 = lane * EPL;
   const T* q = (const T*)a.Q + ((size_t)r * a.hq + h) * DH + e0;
   // window keys: the own keys of the rows of window tokens 0..tw of this state (tw = 0: the

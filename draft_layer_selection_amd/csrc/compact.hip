@@ -1,0 +1,242 @@
+// Live-row plan of a DP item, built on the device between the previous item's select and the
+// item's first GEMM, so that cells pruned by tau or the skip cap (the review's Figure 4:
+// pruning the DP's candidate states cuts its memory and optimisation work) also leave the
+// item's GEMM rows, attention query blocks and partial results.
+//
+// One workgroup of 1024 threads (thread b = budget b):
+//   1. per sequence, a block-wide prefix count over the live candidate sources (valid flag set
+//      and b + w_i <= B - 1) gives each live source its compacted row; the maps of the item
+//      (activation row, sequence, window token, state slot, execute row of the target budget)
+//      are rewritten, the reference follows the sequence's live sources;
+//   2. attention items: each sequence's context split count for its live rows, by the cost
+//      model of the host planner (fewest dispatch rounds x (tiles per workgroup + fixed cost),
+//      ties to fewer workgroups, then to the earlier candidate), every candidate evaluated by a
+//      thread of its own and the minimum taken over the block;
+//   3. the layer's work list: (sequence, KV head, split) groups of query blocks dealt to the
+//      8 dies round-robin (list position p runs on die p % 8), the query blocks of a group
+//      consecutive on its die so the die's L2 serves their shared K/V reads.
+#include "common.h"
+#include "kernels.h"
+
+namespace ks {
+
+namespace {
+
+constexpr int CW = COMPACT_THREADS / 64;  // waves
+
+// Exclusive prefix sum of v over the workgroup (thread order); *total = sum of all v.
+__device__ int block_excl_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < CW; ++w) {
+    const int s = s_wave[w];
+    base += w < wave ? s : 0;
+    tot += s;
+  }
+  __syncthreads();  // s_wave is reused by the next scan
+  *total = tot;
+  return base + x - v;
+}
+
+__device__ unsigned long long block_min_u64(unsigned long long v, unsigned long long* s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned lo = __shfl_xor((unsigned)v, o, 64);
+    const unsigned hi = __shfl_xor((unsigned)(v >> 32), o, 64);
+    const unsigned long long y = ((unsigned long long)hi << 32) | lo;
+    v = y < v ? y : v;
+  }
+  if (lane == 0) s_wave[wave] = v;
+  __syncthreads();
+  unsigned long long m = s_wave[0];
+#pragma unroll
+  for (int w = 1; w < CW; ++w) m = s_wave[w] < m ? s_wave[w] : m;
+  __syncthreads();
+  return m;
+}
+
+// number of i in [0, n) with i % 8 == x
+__device__ __forceinline__ int count_mod8(int n, int x) { return n > x ? (n - x + 7) / 8 : 0; }
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a) {
+  __shared__ int s_wave[CW];
+  __shared__ unsigned long long s_wmin[CW];
+  __shared__ int s_M[COMPACT_MAX_SEQS], s_off[COMPACT_MAX_SEQS];
+  __shared__ int s_qb[COMPACT_MAX_SEQS], s_tiles[COMPACT_MAX_SEQS], s_ns[COMPACT_MAX_SEQS];
+  __shared__ int s_gp[COMPACT_MAX_SEQS + 1];
+  const int tid = threadIdx.x;
+  const int S = a.n_seqs;
+
+  // ---- 1. rows
+  int row_off = 0;
+  for (int q = 0; q < S; ++q) {
+    const int w = a.info[q].w, wr = a.info[q].win;
+    const int next_ref = a.prev_info[q].next_ref_row;
+    const int b = tid;
+    const bool cand = b < a.B && b + w <= a.B - 1;
+    const size_t qb = (size_t)q * a.Bm + b;
+    const bool live = cand && a.valid[qb * a.kmax] != 0;
+    int nlive;
+    const int rank = block_excl_scan(live ? 1 : 0, s_wave, &nlive);
+    const size_t st_q = (size_t)q * (a.Bm + 1) * a.kmax;  // first state slot of the sequence
+    if (cand) {
+      const int row = row_off + rank * wr;
+      a.exec_row[(qb + w) * a.kmax] = live ? row : -1;
+      if (live) {
+        const int prow = a.prev_next_row[qb * a.kmax];
+        for (int t = 0; t < wr; ++t) {
+          a.amap[row + t] = prow + t;
+          a.row_seq[row + t] = q;
+          a.row_tok[row + t] = t;
+          a.row_state[row + t] = (int)((st_q + (size_t)b * a.kmax) * a.wmax + t);
+        }
+      }
+    }
+    const int ref = row_off + nlive * wr;
+    if (tid < wr) {
+      a.amap[ref + tid] = next_ref + tid;
+      a.row_seq[ref + tid] = q;
+      a.row_tok[ref + tid] = tid;
+      a.row_state[ref + tid] = (int)((st_q + (size_t)a.Bm * a.kmax) * a.wmax + tid);
+    }
+    const int M = (nlive + 1) * wr;
+    if (tid == 0) {
+      a.info[q].row_off = row_off;
+      a.info[q].M = M;
+      a.info[q].ref_row = ref;
+      s_M[q] = M;
+      s_off[q] = row_off;
+    }
+    row_off += M;
+  }
+  const int R = row_off;
+  for (int c = R + tid; c < a.R_plan; c += COMPACT_THREADS) {
+    a.amap[c] = 0;
+    a.row_seq[c] = 0;
+    a.row_tok[c] = 0;
+    a.row_state[c] = 0;
+  }
+  if (tid == 0) *a.r_live = R;
+  if (!a.aseq) return;
+  __syncthreads();
+
+  // ---- 2. context splits of the live rows
+  const int G = a.hq / a.hkv;
+  if (tid < S) {
+    s_qb[tid] = ceil_div(G * s_M[tid], a.qb_rows);
+    s_tiles[tid] = ceil_div(a.aseq[tid].ctx, 64);
+  }
+  __syncthreads();
+  int xmin = 1, tmax = 0, qbsum = 0;
+  for (int q = 0; q < S; ++q) {
+    qbsum += s_qb[q];
+    if (s_tiles[q] <= 0) continue;
+    xmin = max(xmin, ceil_div(s_tiles[q], a.max_split));
+    tmax = max(tmax, s_tiles[q]);
+  }
+  // Dealt round-robin, a sequence's n groups give each die floor(n/8) or ceil(n/8) of them,
+  // so a die holds at most count/8 + sum_q qblocks_q entries: the list ends before
+  // count + pad.
+  const long long pad = 8LL * (qbsum + 1);
+  unsigned long long best = ~0ull;
+  const int ncand = 1 + S * a.max_split;
+  for (int ci = tid; ci < ncand && tmax > 0; ci += COMPACT_THREADS) {
+    int x = tmax;
+    if (ci > 0) {
+      const int q = (ci - 1) / a.max_split, k = (ci - 1) % a.max_split + 1;
+      if (s_tiles[q] <= 0) continue;
+      x = ceil_div(s_tiles[q], k);
+    }
+    if (x < xmin || x > tmax) continue;
+    long long count = 0, parts = 0;
+    for (int q = 0; q < S; ++q) {
+      if (s_tiles[q] <= 0) continue;
+      const int ns = ceil_div(s_tiles[q], x);
+      count += (long long)a.hkv * s_qb[q] * ns;
+      parts += (long long)s_M[q] * a.hq * ns;
+    }
+    if (x != tmax && (parts > a.part_cap || count + pad > a.work_cap)) continue;
+    const long long cost = (count + a.slots - 1) / a.slots * (x + 4);
+    if (cost >= (1LL << 24) || count >= (1LL << 28)) continue;  // outside the key's fields
+    const unsigned long long key = ((unsigned long long)cost << 40) |
+                                   ((unsigned long long)count << 12) | (unsigned long long)ci;
+    best = key < best ? key : best;
+  }
+  best = block_min_u64(best, s_wmin);
+  int X = tmax;
+  if (tmax > 0 && best != ~0ull) {
+    const int ci = (int)(best & 4095);
+    if (ci > 0) X = ceil_div(s_tiles[(ci - 1) / a.max_split], (ci - 1) % a.max_split + 1);
+  }
+  if (tid < S) {
+    const int q = tid;
+    const int ctx = a.aseq[q].ctx;
+    const int ns = (s_tiles[q] > 0 && X > 0) ? ceil_div(s_tiles[q], X) : 0;
+    const int chunk = ns > 0 ? ceil_div(s_tiles[q], ns) * 64 : 64;
+    const int nsplit = ctx > 0 ? ceil_div(ctx, chunk) : 0;
+    s_ns[q] = nsplit;
+    AttnSeq* as = a.aseq + q;
+    as->row_off = s_off[q];
+    as->M = s_M[q];
+    as->nsplit = nsplit;
+    as->chunk = chunk;
+    // the smallest multiple of 32 whose s_qb[q] blocks cover the KV head's G*M query rows
+    const int per = s_qb[q] > 0 ? ceil_div(G * s_M[q], s_qb[q]) : 0;
+    as->qrows = (per + 31) / 32 * 32;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long long part = 0;
+    int gp = 0;
+    for (int q = 0; q < S; ++q) {
+      a.aseq[q].part_off = (int)part;
+      part += (long long)s_ns[q] * s_M[q] * a.hq;
+      s_gp[q] = gp;
+      gp += a.hkv * s_ns[q];
+    }
+    s_gp[S] = gp;
+  }
+  // ---- 3. work list
+  for (int p = tid; p < a.work_cap; p += COMPACT_THREADS) a.work[p] = make_int4(-1, 0, 0, 0);
+  __syncthreads();
+  const int ngroups = s_gp[S];
+  for (int g = tid; g < ngroups; g += COMPACT_THREADS) {
+    int q = 0;
+    while (q + 1 < S && s_gp[q + 1] <= g) ++q;
+    const int local = g - s_gp[q];
+    const int c = local / s_ns[q], sp = local % s_ns[q];
+    const int x = g & 7;
+    // entries of die x before this group: the query blocks of the earlier groups dealt to it
+    int off = 0;
+    for (int q2 = 0; q2 < q; ++q2)
+      off += s_qb[q2] * (count_mod8(s_gp[q2 + 1], x) - count_mod8(s_gp[q2], x));
+    off += s_qb[q] * (count_mod8(g, x) - count_mod8(s_gp[q], x));
+    for (int k = 0; k < s_qb[q]; ++k) {
+      const long long p = (long long)(off + k) * 8 + x;
+      if (p < a.work_cap) a.work[p] = make_int4(q, c, k, sp);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  if (a.n_seqs < 1 || a.n_seqs > COMPACT_MAX_SEQS || a.B > COMPACT_THREADS)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(COMPACT_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ks

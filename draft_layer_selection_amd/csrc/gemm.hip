@@ -99,6 +99,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int row0 = mt * 32 * MB;
+  const int rlim = a.r_live ? min(a.R, *a.r_live) : a.R;
+  if (row0 >= rlim) return;
 
   int wrow0, wrow1;
   if (a.mode == GEMM_SWIGLU) {
@@ -119,7 +121,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     int r = row0 + 32 * mb + l32;
-    r = r < a.R ? r : a.R - 1;
+    r = r < rlim ? r : rlim - 1;
+    if (a.amap) r = a.amap[r];
     ap[mb] = A + (size_t)r * a.lda + koff;
   }
   const int nit = (k1 - k0) / 64;
@@ -216,6 +219,9 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int grp = wave / KSL, ksl = wave % KSL;
   const int row0 = mt * 32 * MB;
+  // live-row plan: tiles wholly past the live rows have nothing to compute
+  const int rlim = a.r_live ? min(a.R, *a.r_live) : a.R;
+  if (row0 >= rlim) return;
   const int k0 = sp * a.k_chunk;
   const int k1 = min(a.K, k0 + a.k_chunk);
   const int nit = (k1 - k0) / 64;
@@ -244,7 +250,8 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
       src[j] = W + (size_t)wrow * a.K + k0 + 8 * cglob;
     } else {
       int ar = row0 + (r - WR);
-      ar = ar < a.R ? ar : a.R - 1;
+      ar = ar < rlim ? ar : rlim - 1;
+      if (a.amap) ar = a.amap[ar];
       src[j] = A + (size_t)ar * a.lda + k0 + 8 * cglob;
     }
   }
@@ -428,6 +435,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
   const int row0 = mt * 32;
+  if (a.r_live && row0 >= min(a.R, *a.r_live)) return;
   const float* A = (const float*)a.A;
   const float* W = (const float*)a.W;
 
@@ -442,7 +450,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     for (int e = tid; e < 32 * 32; e += 256) {
       const int r = e >> 5, c = e & 31;
       const int grow = row0 + r, gk = kk + c;
-      As[r][c] = (grow < a.R && gk < k1) ? A[(size_t)grow * a.lda + gk] : 0.f;
+      const int arow = (a.amap && grow < a.R) ? a.amap[grow] : grow;
+      As[r][c] = (grow < a.R && gk < k1) ? A[(size_t)arow * a.lda + gk] : 0.f;
     }
     for (int e = tid; e < 64 * 32; e += 256) {
       const int n = e >> 5, c = e & 31;

@@ -40,6 +40,8 @@ struct GemmArgs {
   int ff;
   int per_xcd;    // ceil(total tiles / 8): XCD-aware tile order
   int ng;         // LDS kernel: 64-column groups per tile (2 or 4); 0 = direct-load kernel
+  const int* amap;    // nullable [R]: A row of output row r is A[amap[r]] (live-row plan)
+  const int* r_live;  // nullable device count: m-tiles starting at or past it are skipped
 };
 
 // Tile/split plan of one GEMM launch (chosen on the host, see plan_gemm).
@@ -167,6 +169,40 @@ struct SelectArgs {
   float* cos_out;          // [S][Bm]
 };
 
+// Live-row plan of one DP item (items 1 .. 2L-1), built on the device from the valid flags
+// that the previous item's select wrote.  A pruned source budget (tau, skip cap) gets no row:
+// sequence q's rows are [live sources in budget order..., reference] x window r, sequences one
+// after another.  Launch sizes stay the ones planned from reachability (R_plan rows); rows at
+// and past the live count get in-range map entries (sequence 0, token 0, state 0, A row 0) so
+// the kernels that process them stay in bounds, and their results are never read.  For an
+// attention item it also picks each sequence's context splits for the live rows (the host
+// planner's cost model: fewest rounds x (tiles + fixed cost), ties to fewer workgroups, then
+// to the earlier candidate) and writes the layer's work list, groups of query blocks dealt to
+// the dies round-robin.
+constexpr int COMPACT_THREADS = 1024;   // one budget per thread: n_budgets <= 1024
+constexpr int COMPACT_MAX_SEQS = 64;
+
+struct CompactArgs {
+  int n_seqs, B, Bm, kmax, wmax;
+  int R_plan;                 // rows the item's launches are sized for
+  const uint8_t* valid;       // [S][Bm][kmax] valid flags before this item (slot 0 used)
+  const int* prev_next_row;   // previous item's next_row: planned activation row of a source
+  const ItemSeq* prev_info;   // previous item's [S] (next_ref_row: planned reference row)
+  ItemSeq* info;              // this item's [S]: row_off, M and ref_row rewritten
+  int* exec_row;              // this item's [S][Bm][kmax]: entries of candidate sources rewritten
+  int* amap;                  // this item's [R_plan] maps
+  int* row_seq;
+  int* row_tok;
+  int* row_state;
+  int* r_live;                // out: rows of live sources and references
+  // attention item only (aseq == nullptr for an MLP item)
+  AttnSeq* aseq;              // the layer's [S]: row_off, M, nsplit, chunk, part_off, qrows
+  int4* work;                 // the layer's work list, work_cap entries (-1 = no work)
+  int work_cap;
+  int hq, hkv, qb_rows, slots, max_split;
+  long long part_cap;
+};
+
 struct InitArgs {
   int n_seqs, Bm, d, mw, wmax, kmax;
   const float* const* x0;  // device array [n_seqs] of device pointers to [r][d]
@@ -211,6 +247,7 @@ hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_init(const InitArgs& a, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 
 // Static device scratch (scratch.hip): STATIC_SCRATCH_BYTES in one file-scope __device__ array
 // per GPU.  resolve_static_scratch takes its device address once per device (call with that

@@ -57,10 +57,12 @@ struct Carver {
 };
 
 // Byte offsets of the per-solve map / launch tables (same layout on host and device).  The
-// attention work lists come last so that a solve uploads only the part it filled.
+// attention work lists come after the host-built tables so that a solve uploads only the part
+// it filled; the live-row plan's activation-row maps and live counts, written on the device
+// only, come last.
 struct MapLayout {
-  size_t exec, next, rowseq, rowstate, rowtok, info, work, aseq, rope, x0, init, total,
-      max_work;
+  size_t exec, next, rowseq, rowstate, rowtok, info, work, aseq, rope, x0, init, amap, rlive,
+      total, max_work;
 };
 
 MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int hkv, int G,
@@ -82,6 +84,8 @@ MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int
   const size_t qb_max = (G * (Bm + 1) * wmax * kmax + 63) / 64;
   L.max_work = (size_t)n_layers * (S * hkv * qb_max * asplit_max + N_XCD * qb_max);
   L.work = c.take(L.max_work * 16);
+  L.amap = c.take((size_t)L2 * Rmax * 4);
+  L.rlive = c.take((size_t)L2 * 4);
   L.total = c.off;
   return L;
 }
@@ -702,6 +706,14 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     return fail(KNAPSPEC_EINVAL, "per-cell decisions and margins need beam <= 1");
   if (use_lm && !m->lm_w)
     return fail(KNAPSPEC_EINVAL, "KNAPSPEC_ALPHA_LM_HEAD set but no LM head (knapspec_set_lm_head)");
+  // Live-row plan: with tau or skip-cap pruning on, the rows of every item after the first are
+  // rebuilt on the device from the previous item's valid flags (compact_kernel), so a pruned
+  // budget leaves the item's GEMMs, attention and partial results.  One-state DP, up to
+  // COMPACT_MAX_SEQS sequences; KNAPSPEC_KEEP_PRUNED_ROWS keeps the rows planned from
+  // reachability instead.
+  const bool pruning = args->tau > -INFINITY || args->max_skip_weight >= 0;
+  const bool compact = pruning && K == 1 && S <= ks::COMPACT_MAX_SEQS &&
+                       B <= ks::COMPACT_THREADS && !(args->flags & KNAPSPEC_KEEP_PRUNED_ROWS);
   for (int q = 0; q < S; ++q) {
     const knapspec_seq& sq = args->seqs[q];
     if (sq.ctx_len < 0 || sq.ctx_len > d.max_ctx)
@@ -737,9 +749,9 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
   }
 
   // ---- per-sequence weights and budget reachability.  Rows are planned from reachability,
-  //      which does not depend on the data; tau and skip-cap pruning act on the device (the
-  //      select kernel invalidates cells), so a pruned budget keeps its rows in later items'
-  //      GEMMs and attention: pruning changes results, not the work done.
+  //      which does not depend on the data: these plans size every launch.  Pruning acts on
+  //      the device (the select kernel invalidates cells); with the live-row plan the rows of
+  //      items after the first are then rebuilt on the device without the pruned budgets.
   std::vector<SeqPlan> plan(S);
   for (int q = 0; q < S; ++q) {
     SeqPlan& p = plan[q];
@@ -846,8 +858,8 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
   // other dies' positions in a round are filled with empty entries.
   std::vector<int> work_off(d.n_layers), work_cnt(d.n_layers);
   size_t nw = 0;
+  const int slots = m->n_cus * ks::attention_wgs_per_cu(m->act, dh);
   {
-    const int slots = m->n_cus * ks::attention_wgs_per_cu(m->act, dh);
     std::vector<int> pairs(S), tiles(S), qblocks(S), nsplit;
     std::vector<size_t> prow(S);
     std::vector<std::vector<int4>> die(N_XCD);
@@ -893,6 +905,20 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       }
       if (part > m->part_slots)
         return fail(KNAPSPEC_EINVAL, "internal: attention partial slots overflow");
+      if (compact && l > 0) {
+        // the live-row plan writes this layer's list on the device: reserve room for any
+        // split choice it may make (at most the larger of one dispatch round and the
+        // unsplit pairs, plus the die round-robin's padding) -- placed after the host lists
+        size_t need = 0, qbs = 0;
+        for (int q = 0; q < S; ++q) {
+          if (tiles[q] > 0) need += (size_t)pairs[q];
+          qbs += (size_t)qblocks[q];
+        }
+        const size_t pad = 8 * (qbs + 1);
+        const size_t bound = max_work / (size_t)d.n_layers;
+        work_cnt[l] = (int)std::max(need + pad, std::min(std::max(need, (size_t)slots) + pad, bound));
+        continue;
+      }
       work_off[l] = (int)nw;
       const size_t rounds = *std::max_element(load.begin(), load.end());
       if (nw + rounds * N_XCD > max_work)
@@ -903,6 +929,14 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       // drop the trailing empty entries of the last round
       while (nw > (size_t)work_off[l] && work[nw - 1].x < 0) --nw;
       work_cnt[l] = (int)nw - work_off[l];
+    }
+    if (compact) {
+      size_t off = nw;
+      for (int l = 1; l < d.n_layers; ++l) {
+        work_off[l] = (int)off;
+        off += (size_t)work_cnt[l];
+      }
+      if (off > max_work) return fail(KNAPSPEC_EINVAL, "internal: attention work list overflow");
     }
   }
   // RoPE tables at positions ctx_len + t of each sequence's window tokens:
@@ -949,6 +983,8 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
   const int4* d_work = (const int4*)(dm + o_work);
   const ks::AttnSeq* d_aseq = (const ks::AttnSeq*)(dm + o_aseq);
   const float* d_rope = (const float*)(dm + o_rope);
+  int32_t* d_amap = (int32_t*)(dm + ml.amap);
+  int32_t* d_rlive = (int32_t*)(dm + ml.rlive);
 
   // ---- DP start
   int cur = 0;
@@ -975,11 +1011,13 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
 
   auto gemm = [&](const void* A, int lda, int R, const void* W, int K, int N, int mode,
-                  int* splits_out, int kclass) -> int {
+                  int* splits_out, int kclass, const int* amap = nullptr,
+                  const int* r_live = nullptr) -> int {
     ks::GemmArgs g{};
     g.A = A;
     g.lda = lda;
     g.R = R;
+    g.amap = amap;
     g.W = W;
     g.K = K;
     g.N = N;
@@ -991,6 +1029,7 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     g.n_tiles = p.n_tiles;
     g.splits = p.splits;
     g.k_chunk = p.k_chunk;
+    g.r_live = p.m_tiles > 1 ? r_live : nullptr;  // one m-tile always holds a live row
     if (mode == ks::GEMM_SWIGLU) {
       g.H = m->h;
       g.ldh = d.d_ff;
@@ -1012,8 +1051,45 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     const knapspec_layer_weights& W = m->layers[l];
     int splits = 1;
     int rc;
+    const bool live_plan = compact && i > 0;
+    const int* amap = live_plan ? d_amap + (size_t)i * m->Rmax : nullptr;
+    const int* r_live = live_plan ? d_rlive + i : nullptr;
+    if (live_plan) {
+      ks::CompactArgs pa{};
+      pa.n_seqs = S;
+      pa.B = B;
+      pa.Bm = Bm;
+      pa.kmax = Kb;
+      pa.wmax = Wm;
+      pa.R_plan = R;
+      pa.valid = m->valid[cur];
+      pa.prev_next_row = d_next + (size_t)(i - 1) * S * Bm * Kb;
+      pa.prev_info = d_info + (size_t)(i - 1) * S;
+      pa.info = (ks::ItemSeq*)(dm + o_info) + (size_t)i * S;
+      pa.exec_row = (int32_t*)(dm + o_exec) + (size_t)i * S * Bm * Kb;
+      pa.amap = d_amap + (size_t)i * m->Rmax;
+      pa.row_seq = (int32_t*)(dm + o_rowseq) + (size_t)i * m->Rmax;
+      pa.row_tok = (int32_t*)(dm + o_rowtok) + (size_t)i * m->Rmax;
+      pa.row_state = (int32_t*)(dm + o_rowstate) + (size_t)i * m->Rmax;
+      pa.r_live = d_rlive + i;
+      if (i % 2 == 0) {
+        pa.aseq = (ks::AttnSeq*)(dm + o_aseq) + (size_t)l * S;
+        pa.work = (int4*)(dm + o_work) + work_off[l];
+        pa.work_cap = work_cnt[l];
+        pa.hq = hq;
+        pa.hkv = hkv;
+        pa.qb_rows = (int)qb_rows;
+        pa.slots = slots;
+        pa.max_split = ASPLIT_MAX;
+        pa.part_cap = (long long)m->part_slots;
+      }
+      const int pk = prof_begin(m, KNAPSPEC_K_SELECT, st);
+      HIPCHK(ks::launch_compact(pa, st));
+      prof_end(m, pk, st);
+    }
     if (i % 2 == 0) {
-      rc = gemm(m->xa, D, R, W.w_qkv, D, m->nqkv, ks::GEMM_PARTIAL, &splits, KNAPSPEC_K_GEMM_QKV);
+      rc = gemm(m->xa, D, R, W.w_qkv, D, m->nqkv, ks::GEMM_PARTIAL, &splits, KNAPSPEC_K_GEMM_QKV,
+                amap, r_live);
       if (rc) return rc;
       ks::QkvArgs qa{};
       qa.P = m->P;
@@ -1067,15 +1143,16 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       pk = prof_begin(m, KNAPSPEC_K_COMBINE, st);
       HIPCHK(ks::launch_combine(ca, m->act, st));
       prof_end(m, pk, st);
-      rc = gemm(m->o, m->qdim, R, W.w_o, m->qdim, D, ks::GEMM_PARTIAL, &splits, KNAPSPEC_K_GEMM_O);
+      rc = gemm(m->o, m->qdim, R, W.w_o, m->qdim, D, ks::GEMM_PARTIAL, &splits, KNAPSPEC_K_GEMM_O,
+                nullptr, r_live);
       if (rc) return rc;
     } else {
       int s1 = 1;
       rc = gemm(m->xa, D, R, W.w_gate_up, D, 2 * d.d_ff, ks::GEMM_SWIGLU, &s1,
-                KNAPSPEC_K_GEMM_GATE_UP);
+                KNAPSPEC_K_GEMM_GATE_UP, amap, r_live);
       if (rc) return rc;
       rc = gemm(m->h, d.d_ff, R, W.w_down, d.d_ff, D, ks::GEMM_PARTIAL, &splits,
-                KNAPSPEC_K_GEMM_DOWN);
+                KNAPSPEC_K_GEMM_DOWN, nullptr, r_live);
       if (rc) return rc;
     }
     ks::ReduceArgs ra{};

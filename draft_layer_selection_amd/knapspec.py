@@ -27,6 +27,7 @@ KNAPSPEC_BF16 = 1
 KNAPSPEC_RETURN_DECISIONS = 1
 KNAPSPEC_RETURN_MARGINS = 2
 KNAPSPEC_ALPHA_LM_HEAD = 4
+KNAPSPEC_KEEP_PRUNED_ROWS = 8
 KNAPSPEC_WINDOW_MAX = 16
 KNAPSPEC_BEAM_MAX = 8
 KERNEL_CLASSES = ["init", "gemm_qkv", "qkv_rope", "attention", "combine", "gemm_o",

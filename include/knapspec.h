@@ -54,6 +54,7 @@ extern "C" {
 #define KNAPSPEC_RETURN_DECISIONS 1 /* fill knapspec_result.decisions */
 #define KNAPSPEC_RETURN_MARGINS 2   /* fill knapspec_result.margins */
 #define KNAPSPEC_ALPHA_LM_HEAD 4    /* TPT acceptance from the LM head (knapspec_set_lm_head) */
+#define KNAPSPEC_KEEP_PRUNED_ROWS 8 /* keep the rows of pruned budgets (see knapspec_solve) */
 
 #define KNAPSPEC_WINDOW_MAX 16 /* largest r of an r-token window */
 #define KNAPSPEC_BEAM_MAX 8   /* largest beam width of the beam variant of the DP */
@@ -135,7 +136,7 @@ typedef struct {
   float tau;                  /* prune a cell whose kept cosine < tau; -INFINITY disables */
   int32_t max_skip_weight;    /* prune cells whose skipped weight P_i - b exceeds it; <0 off */
   int32_t flags;              /* KNAPSPEC_RETURN_DECISIONS | KNAPSPEC_RETURN_MARGINS |
-                                 KNAPSPEC_ALPHA_LM_HEAD */
+                                 KNAPSPEC_ALPHA_LM_HEAD | KNAPSPEC_KEEP_PRUNED_ROWS */
   void* hip_stream;           /* stream the work is enqueued on (NULL = default stream) */
   int32_t beam;               /* states kept per (item, budget) cell: 0 or 1 = the one-state
                                  DP; k in 2..desc.max_beam = the beam variant (review,

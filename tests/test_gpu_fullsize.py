@@ -65,8 +65,9 @@ def check_structure(res, q, t, B, gamma, n_items, t_target, decisions=True, alph
     assert (pick[0], pick[1]) == (int(res.best_budget[q]), int(res.best_gamma[q]))
 
 
-def full_parity(layers, prob, res, q, wl, ctx, x0, label=""):
-    """The oracle's whole solve for sequence q against the GPU's (P1-P4 on every cell)."""
+def full_parity(layers, prob, res, q, wl, ctx, x0, label="", tau=-math.inf, skip_cap=-1):
+    """The oracle's whole solve for sequence q against the GPU's (P1-P4 on every cell), with
+    the same tau / skip-cap pruning."""
     from tests.helpers import LockstepSubsets
     from tests.parity import compare
 
@@ -80,7 +81,7 @@ def full_parity(layers, prob, res, q, wl, ctx, x0, label=""):
     lock = LockstepSubsets(items, x0, bits)
     t0 = time.time()
     orc = ko.solve(decoder_shape(wl), None, None, x0, ctx, lat, wl.n_budgets, wl.gamma,
-                   apply_item=lock)
+                   tau=tau, skip_cap=skip_cap, apply_item=lock)
     p2 = np.full(wl.n_budgets, np.nan)
     p2[valid] = lock.cos(orc.dp.ref)
     rep = compare(orc, res, q, BETA[s.dtype], None, x0, wl.gamma, n_items, p2_cos=p2)

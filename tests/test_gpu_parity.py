@@ -18,17 +18,18 @@ pytestmark = pytest.mark.gpu
 BETA = {"f32": 1e-5, "bf16": 2e-3}
 
 
-def run_case(wl, seed=0, ctxs=None, tau=-math.inf, cap=-1, n_budgets=None, per_item=None):
+def run_case(wl, seed=0, ctxs=None, tau=-math.inf, cap=-1, n_budgets=None, per_item=None,
+             flags=3):
     from workloads.device import DeviceProblem
 
     print(f"\n[case] {wl.name} L={wl.shape.n_layers} d={wl.shape.d_model} "
           f"hq/hkv={wl.shape.n_q_heads}/{wl.shape.n_kv_heads} dh={wl.shape.head_dim} "
-          f"dtype={wl.shape.dtype} ctxs={ctxs} B={n_budgets or wl.n_budgets} tau={tau} cap={cap}",
-          flush=True)
+          f"dtype={wl.shape.dtype} ctxs={ctxs} B={n_budgets or wl.n_budgets} tau={tau} cap={cap} "
+          f"flags={flags}", flush=True)
     prob = DeviceProblem(wl, seed, ctxs=ctxs, keep_host=True,
                          max_budgets=n_budgets or wl.n_budgets)
     B = n_budgets or wl.n_budgets
-    res = prob.solve(n_budgets=B, tau=tau, max_skip_weight=cap, flags=3)
+    res = prob.solve(n_budgets=B, tau=tau, max_skip_weight=cap, flags=flags)
     beta = BETA[wl.shape.dtype]
     n_items = 2 * wl.shape.n_layers
     lat = {"attn_base": wl.latency.attn_base, "attn_per_token": wl.latency.attn_per_token,

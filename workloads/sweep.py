@@ -87,26 +87,33 @@ def context_sweep(prob, ctx_list: Sequence[int], n_budgets: Optional[int] = None
 def tau_ablation(prob, taus: Sequence[float], reps: int = 5, n_budgets: Optional[int] = None,
                  gamma=None) -> List[dict]:
     """Solve time (median of reps, host clock around the synchronous solve) and live states
-    per item (cells whose decision is not 'invalid') for each tau."""
+    per item (cells whose decision is not 'invalid') for each tau.  With pruning on, the solve
+    drops pruned budgets' rows on the device; ``solve_ms_kept_rows`` times the same solve with
+    the rows planned from reachability kept (KNAPSPEC_KEEP_PRUNED_ROWS)."""
     import torch
 
     wl = prob.wl
     n_items = 2 * wl.shape.n_layers
+    keep = prob.ks.KNAPSPEC_KEEP_PRUNED_ROWS
+
+    def timed(tau, flags):
+        for _ in range(2):  # untimed: the first solves of a configuration capture its graph
+            prob.solve(n_budgets=n_budgets, gamma=gamma, tau=tau, flags=flags)
+        times = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            prob.solve(n_budgets=n_budgets, gamma=gamma, tau=tau, flags=flags)
+            times.append(time.perf_counter() - t0)
+        return 1e3 * float(np.median(times))
+
     rows = []
     for tau in taus:
         res = prob.solve(n_budgets=n_budgets, gamma=gamma, tau=tau, flags=1)  # decisions
         dec = res.decisions[0]
         live = (dec != 255).sum(axis=1)
-        for _ in range(2):  # untimed: the first solves of a configuration capture its graph
-            prob.solve(n_budgets=n_budgets, gamma=gamma, tau=tau)
-        times = []
-        for _ in range(reps):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            prob.solve(n_budgets=n_budgets, gamma=gamma, tau=tau)
-            times.append(time.perf_counter() - t0)
         row = {"tau": None if math.isinf(tau) else float(tau),
-               "solve_ms": 1e3 * float(np.median(times)),
+               "solve_ms": timed(tau, 0), "solve_ms_kept_rows": timed(tau, keep),
                "live_states_mean": float(live.mean()), "live_states_last": int(live[-1])}
         row.update(layer_set_stats(res, 0, n_items))
         rows.append(row)
