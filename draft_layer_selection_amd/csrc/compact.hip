@@ -24,6 +24,12 @@ namespace {
 
 constexpr int CW = COMPACT_THREADS / 64;  // waves
 
+// Barrier for LDS traffic only: the kernel's global stores are never read back by it, so the
+// barrier does not wait for them (a full __syncthreads waits for every store in flight).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Exclusive prefix sum of v over the workgroup (thread order); *total = sum of all v.
 __device__ int block_excl_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -34,7 +40,7 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
     if (lane >= o) x += y;
   }
   if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
+  lds_sync();
   int base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < CW; ++w) {
@@ -42,7 +48,7 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
     base += w < wave ? s : 0;
     tot += s;
   }
-  __syncthreads();  // s_wave is reused by the next scan
+  lds_sync();  // s_wave is reused by the next scan
   *total = tot;
   return base + x - v;
 }
@@ -57,11 +63,10 @@ __device__ unsigned long long block_min_u64(unsigned long long v, unsigned long 
     v = y < v ? y : v;
   }
   if (lane == 0) s_wave[wave] = v;
-  __syncthreads();
+  lds_sync();
   unsigned long long m = s_wave[0];
 #pragma unroll
   for (int w = 1; w < CW; ++w) m = s_wave[w] < m ? s_wave[w] : m;
-  __syncthreads();
   return m;
 }
 
@@ -76,8 +81,11 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
   __shared__ int s_M[COMPACT_MAX_SEQS], s_off[COMPACT_MAX_SEQS];
   __shared__ int s_qb[COMPACT_MAX_SEQS], s_tiles[COMPACT_MAX_SEQS], s_ns[COMPACT_MAX_SEQS];
   __shared__ int s_gp[COMPACT_MAX_SEQS + 1];
+  __shared__ int s_load[8];
   const int tid = threadIdx.x;
   const int S = a.n_seqs;
+  // the layer's context lengths, loaded with the first sequence's inputs
+  const int ctx_t = (a.aseq && tid < S) ? a.aseq[tid].ctx : 0;
 
   // ---- 1. rows
   int row_off = 0;
@@ -85,9 +93,13 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
     const int w = a.info[q].w, wr = a.info[q].win;
     const int next_ref = a.prev_info[q].next_ref_row;
     const int b = tid;
-    const bool cand = b < a.B && b + w <= a.B - 1;
     const size_t qb = (size_t)q * a.Bm + b;
-    const bool live = cand && a.valid[qb * a.kmax] != 0;
+    // loads of every budget of the sequence (in range for b < B), independent of w
+    const bool inb = b < a.B;
+    const int vflag = inb ? a.valid[qb * a.kmax] : 0;
+    const int prow = inb ? a.prev_next_row[qb * a.kmax] : 0;
+    const bool cand = inb && b + w <= a.B - 1;
+    const bool live = cand && vflag != 0;
     int nlive;
     const int rank = block_excl_scan(live ? 1 : 0, s_wave, &nlive);
     const size_t st_q = (size_t)q * (a.Bm + 1) * a.kmax;  // first state slot of the sequence
@@ -95,7 +107,6 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
       const int row = row_off + rank * wr;
       a.exec_row[(qb + w) * a.kmax] = live ? row : -1;
       if (live) {
-        const int prow = a.prev_next_row[qb * a.kmax];
         for (int t = 0; t < wr; ++t) {
           a.amap[row + t] = prow + t;
           a.row_seq[row + t] = q;
@@ -130,15 +141,15 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
   }
   if (tid == 0) *a.r_live = R;
   if (!a.aseq) return;
-  __syncthreads();
 
   // ---- 2. context splits of the live rows
   const int G = a.hq / a.hkv;
+  lds_sync();  // s_M, s_off
   if (tid < S) {
     s_qb[tid] = ceil_div(G * s_M[tid], a.qb_rows);
-    s_tiles[tid] = ceil_div(a.aseq[tid].ctx, 64);
+    s_tiles[tid] = ceil_div(ctx_t, 64);
   }
-  __syncthreads();
+  lds_sync();
   int xmin = 1, tmax = 0, qbsum = 0;
   for (int q = 0; q < S; ++q) {
     qbsum += s_qb[q];
@@ -180,12 +191,12 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
     const int ci = (int)(best & 4095);
     if (ci > 0) X = ceil_div(s_tiles[(ci - 1) / a.max_split], (ci - 1) % a.max_split + 1);
   }
+  int nsplit = 0;
   if (tid < S) {
     const int q = tid;
-    const int ctx = a.aseq[q].ctx;
     const int ns = (s_tiles[q] > 0 && X > 0) ? ceil_div(s_tiles[q], X) : 0;
     const int chunk = ns > 0 ? ceil_div(s_tiles[q], ns) * 64 : 64;
-    const int nsplit = ctx > 0 ? ceil_div(ctx, chunk) : 0;
+    nsplit = ctx_t > 0 ? ceil_div(ctx_t, chunk) : 0;
     s_ns[q] = nsplit;
     AttnSeq* as = a.aseq + q;
     as->row_off = s_off[q];
@@ -196,7 +207,7 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
     const int per = s_qb[q] > 0 ? ceil_div(G * s_M[q], s_qb[q]) : 0;
     as->qrows = (per + 31) / 32 * 32;
   }
-  __syncthreads();
+  lds_sync();  // s_ns
   if (tid == 0) {
     long long part = 0;
     int gp = 0;
@@ -208,9 +219,18 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
     }
     s_gp[S] = gp;
   }
-  // ---- 3. work list
-  for (int p = tid; p < a.work_cap; p += COMPACT_THREADS) a.work[p] = make_int4(-1, 0, 0, 0);
-  __syncthreads();
+  lds_sync();  // s_gp
+  if (tid < 8) {  // entries dealt to die x
+    int ld = 0;
+    for (int q = 0; q < S; ++q)
+      ld += s_qb[q] * (count_mod8(s_gp[q + 1], tid) - count_mod8(s_gp[q], tid));
+    s_load[tid] = ld;
+  }
+  lds_sync();  // s_load
+
+  // ---- 3. work list: positions past a die's entries are empty, the rest hold the groups
+  for (int p = tid; p < a.work_cap; p += COMPACT_THREADS)
+    if ((p >> 3) >= s_load[p & 7]) a.work[p] = make_int4(-1, 0, 0, 0);
   const int ngroups = s_gp[S];
   for (int g = tid; g < ngroups; g += COMPACT_THREADS) {
     int q = 0;

@@ -42,6 +42,7 @@ constexpr int PSPLIT_MAX = 8;    // K splits of the partial-output GEMMs
 constexpr int ASPLIT_MAX = 32;   // context splits of the attention (combine: <= 64)
 constexpr int N_XCD = 8;         // accelerator complex dies; workgroup i runs on die i % 8
 constexpr int MAX_BUDGETS = 1024;
+constexpr int LIVE_PLAN_MLP_ROWS = 512;  // MLP items with more planned rows get a live-row plan
 constexpr int GAMMA_LIMIT = 64;
 constexpr size_t ALIGN = 256;
 
@@ -1051,7 +1052,11 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     const knapspec_layer_weights& W = m->layers[l];
     int splits = 1;
     int rc;
-    const bool live_plan = compact && i > 0;
+    // Attention items always (the attention's work grows with the rows); MLP items only with
+    // enough rows for the GEMMs to be bound by rows rather than by their weight stream --
+    // below that a dropped row saves nothing and the plan's launch would be pure cost.
+    // Either way the select writes the next item's activation rows at their planned places.
+    const bool live_plan = compact && i > 0 && (i % 2 == 0 || R > LIVE_PLAN_MLP_ROWS);
     const int* amap = live_plan ? d_amap + (size_t)i * m->Rmax : nullptr;
     const int* r_live = live_plan ? d_rlive + i : nullptr;
     if (live_plan) {

@@ -1,8 +1,9 @@
 """knapspec_solve_static (per-solve device buffers in the library's static scratch, no
 allocation) against knapspec_solve on the same inputs: two calls in a row, the second with a
 smaller input (fewer budgets, shorter context, another x0), each compared bit for bit with
-knapspec_solve's output on the same input (same kernels, deterministic).  Also: a model whose
-per-solve buffers exceed the static scratch is refused with EINVAL."""
+knapspec_solve's output on the same input (same kernels, deterministic); then a third call with
+tau pruning on, whose live-row plan builds its row maps in the static array too.  Also: a model
+whose per-solve buffers exceed the static scratch is refused with EINVAL."""
 import math
 
 import numpy as np
@@ -48,6 +49,10 @@ def test_static_scratch_solve_matches_solve(wl):
                            static_scratch=True)
     same(st2, ref2)
     assert not np.array_equal(st1.cos[0][: small["n_budgets"]], st2.cos[0])
+    ref3 = prob.solve(n_budgets=B, tau=0.5, flags=3, ctxs=[300])
+    st3 = prob.model.solve(prob.seq_args([300]), B, wl.gamma, 0.5, -1, 3, static_scratch=True)
+    same(st3, ref3)
+    assert st3.valid[0].sum() <= ref1.valid[0].sum()  # pruning only removes budgets
     print(f"  static == solve on both calls: picks {(int(st1.best_budget[0]), int(st1.best_gamma[0]))}"
           f" and {(int(st2.best_budget[0]), int(st2.best_gamma[0]))}", flush=True)
     prob.close()

@@ -207,6 +207,10 @@ def main(argv=None):
                     help="also solve the sweep with the measured (fitted) latency model")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--out", default="")
+    ap.add_argument("--solves", type=int, default=0, metavar="N",
+                    help="only run N solves at each tau of --taus (e.g. under a kernel tracer)")
+    ap.add_argument("--kept-rows", action="store_true",
+                    help="with --solves: keep the pruned budgets' rows (KNAPSPEC_KEEP_PRUNED_ROWS)")
     args = ap.parse_args(argv)
 
     from .device import DeviceProblem
@@ -220,6 +224,19 @@ def main(argv=None):
     beams = [int(x) for x in args.beams.split(",")] if args.beams else []
     prob = DeviceProblem(wl, args.seed, ctxs=[wl.ctx], caps=[cap],
                          max_beam=max(beams) if beams else 1, lm_vocab=args.draft_verify)
+    if args.solves:
+        import torch
+
+        flags = prob.ks.KNAPSPEC_KEEP_PRUNED_ROWS if args.kept_rows else 0
+        for tau in taus:
+            for k in range(args.solves):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                prob.solve(tau=tau, flags=flags)
+                print(f"tau {tau} solve {k}: {1e3 * (time.perf_counter() - t0):.3f} ms",
+                      flush=True)
+        prob.close()
+        return
     out = {"workload": wl.name, "layers": wl.shape.n_layers, "n_budgets": wl.n_budgets,
            "latency_model": "bandwidth-bound stand-in (8 TB/s)",
            "sweep": context_sweep(prob, ctx_list)}
