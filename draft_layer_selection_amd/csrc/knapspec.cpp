@@ -198,6 +198,10 @@ struct knapspec_model {
   std::vector<hipEvent_t> events;
   std::vector<int> ev_class;
   int ev_used = 0;
+  // host planning buffers reused by every solve (capacity kept, so steady-state solves do not
+  // allocate on the host)
+  std::vector<std::vector<int32_t>> plan_src;   // [S * L2] source slots of (sequence, item)
+  std::vector<std::vector<int4>> plan_die;      // [N_XCD] attention work per die
   double k_ms[KNAPSPEC_KERNEL_CLASSES] = {};
   int64_t k_count[KNAPSPEC_KERNEL_CLASSES] = {};
 
@@ -669,8 +673,9 @@ struct SeqPlan {
   std::vector<double> t;
   std::vector<int32_t> w;
   std::vector<int> prefix;
-  // src[i] = source slots of item i as budget * kmax + beam slot, by budget then slot
-  std::vector<std::vector<int>> src;
+  // src[i] = source slots of item i as budget * kmax + beam slot, by budget then slot (the
+  // model's reused buffers)
+  std::vector<int32_t>* src = nullptr;
 };
 
 }  // namespace
@@ -754,6 +759,7 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
   //      the device (the select kernel invalidates cells); with the live-row plan the rows of
   //      items after the first are then rebuilt on the device without the pruned budgets.
   std::vector<SeqPlan> plan(S);
+  if (m->plan_src.size() < (size_t)S * L2) m->plan_src.resize((size_t)S * L2);
   for (int q = 0; q < S; ++q) {
     SeqPlan& p = plan[q];
     p.t.resize(L2);
@@ -761,7 +767,8 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     int rc = item_weights(&m->lat, d.n_layers, args->seqs[q].ctx_len, B, p.t.data(), p.w.data());
     if (rc) return rc;
     p.prefix.resize(L2);
-    p.src.resize(L2);
+    p.src = m->plan_src.data() + (size_t)q * L2;
+    for (int i = 0; i < L2; ++i) p.src[i].clear();
     // states per budget before item i (distinct subsets of that weight, capped at the beam;
     // 0/1 = reachability for the one-state DP)
     std::vector<int> cnt(B, 0), nxt(B);
@@ -863,7 +870,8 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
   {
     std::vector<int> pairs(S), tiles(S), qblocks(S), nsplit;
     std::vector<size_t> prow(S);
-    std::vector<std::vector<int4>> die(N_XCD);
+    if (m->plan_die.size() < (size_t)N_XCD) m->plan_die.resize(N_XCD);
+    std::vector<std::vector<int4>>& die = m->plan_die;
     for (int l = 0; l < d.n_layers; ++l) {
       const int i = 2 * l;
       for (int q = 0; q < S; ++q) {
