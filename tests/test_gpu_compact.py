@@ -10,8 +10,9 @@ leave the GEMMs, the attention and its partial results.
 * Everything pruned after the first item (tau = 1.5): only the reference rows stay; results
   are bit-identical too (all budgets invalid).
 * Pruned for real (tau = 0.5, a skip cap): both plans pass parity against the oracle's DP
-  with the same pruning, one and several sequences; the full Qwen3-1.7B preset and the
-  Llama-3-8B 32K preset at tau = 0.5 against the oracle's whole DP.
+  with the same pruning, one and several sequences (4 sequences x 200 budgets puts more than
+  512 rows in every item, so the MLP items get live-row plans too); the full Qwen3-1.7B preset
+  and the Llama-3-8B 32K preset at tau = 0.5 against the oracle's whole DP.
 """
 import math
 
@@ -75,6 +76,16 @@ def test_nothing_pruned_bf16_three_sequences():
 
 def test_nothing_pruned_window3_skip_cap():
     _bit_equal(WORKLOADS["tiny"], [100, 40], cap=10 ** 6, window=3)
+
+
+def test_nothing_pruned_mlp_items_planned_too():
+    # 4 sequences x 200 budgets: items hold more than 512 rows, so MLP items get a live-row
+    # plan as well (their GEMMs skip m-tiles past the live rows)
+    _bit_equal(WORKLOADS["tiny"], [256, 100, 31, 0], tau=-2.0, n_budgets=200)
+
+
+def test_pruned_parity_mlp_items_planned_too():
+    run_case(WORKLOADS["tiny"], ctxs=[256, 100, 31, 0], tau=0.3, n_budgets=200)
 
 
 def test_everything_pruned_after_first_item():
