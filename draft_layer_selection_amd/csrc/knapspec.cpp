@@ -201,7 +201,6 @@ struct knapspec_model {
   // host planning buffers reused by every solve (capacity kept, so steady-state solves do not
   // allocate on the host)
   std::vector<std::vector<int32_t>> plan_src;   // [S * L2] source slots of (sequence, item)
-  std::vector<std::vector<int4>> plan_die;      // [N_XCD] attention work per die
   double k_ms[KNAPSPEC_KERNEL_CLASSES] = {};
   int64_t k_count[KNAPSPEC_KERNEL_CLASSES] = {};
 
@@ -862,16 +861,16 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
   }
   // attention work lists, one per attention item, in item order.  The query blocks of one
   // (sequence, KV head, split) read the same keys and values: they are placed on one die
-  // (list positions congruent mod N_XCD) so the die's L2 serves the repeated reads; the
-  // other dies' positions in a round are filled with empty entries.
+  // (list positions congruent mod N_XCD) so the die's L2 serves the repeated reads.  The
+  // groups are dealt to the dies round-robin in (sequence, KV head, split) order -- with 8 KV
+  // heads every die gets the same share of each sequence -- and the other dies' positions in
+  // a round are filled with empty entries.  The live-row plan builds its lists the same way.
   std::vector<int> work_off(d.n_layers), work_cnt(d.n_layers);
   size_t nw = 0;
   const int slots = m->n_cus * ks::attention_wgs_per_cu(m->act, dh);
   {
     std::vector<int> pairs(S), tiles(S), qblocks(S), nsplit;
     std::vector<size_t> prow(S);
-    if (m->plan_die.size() < (size_t)N_XCD) m->plan_die.resize(N_XCD);
-    std::vector<std::vector<int4>>& die = m->plan_die;
     for (int l = 0; l < d.n_layers; ++l) {
       const int i = 2 * l;
       for (int q = 0; q < S; ++q) {
@@ -883,8 +882,8 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       }
       plan_attention_splits(pairs, tiles, prow, slots, ASPLIT_MAX, m->part_slots, nsplit);
       size_t part = 0;
-      for (auto& v : die) v.clear();
-      std::vector<size_t> load(N_XCD, 0);
+      size_t load[N_XCD] = {0};  // query blocks dealt to each die
+      int g = 0;                  // group index: (sequence, KV head, split) in that order
       for (int q = 0; q < S; ++q) {
         const knapspec_seq& sq = args->seqs[q];
         const int M = ((int)plan[q].src[i].size() + 1) * win[q];
@@ -905,12 +904,7 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
         as.qrows = balanced_qrows(G * M, qblocks[q]);
         as.pad2 = 0;
         part += (size_t)as.nsplit * M * hq;
-        for (int c = 0; c < hkv; ++c)
-          for (int sp = 0; sp < as.nsplit; ++sp) {
-            const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-            for (int qb = 0; qb < qblocks[q]; ++qb) die[x].push_back(make_int4(q, c, qb, sp));
-            load[x] += qblocks[q];
-          }
+        for (int k = 0; k < hkv * as.nsplit; ++k, ++g) load[g % N_XCD] += (size_t)qblocks[q];
       }
       if (part > m->part_slots)
         return fail(KNAPSPEC_EINVAL, "internal: attention partial slots overflow");
@@ -929,12 +923,23 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
         continue;
       }
       work_off[l] = (int)nw;
-      const size_t rounds = *std::max_element(load.begin(), load.end());
+      const size_t rounds = *std::max_element(load, load + N_XCD);
       if (nw + rounds * N_XCD > max_work)
         return fail(KNAPSPEC_EINVAL, "internal: attention work list overflow");
-      for (size_t j = 0; j < rounds; ++j)
-        for (int x = 0; x < N_XCD; ++x)
-          work[nw++] = j < die[x].size() ? die[x][j] : make_int4(-1, 0, 0, 0);
+      std::fill(work + nw, work + nw + rounds * N_XCD, make_int4(-1, 0, 0, 0));
+      size_t off[N_XCD] = {0};
+      g = 0;
+      for (int q = 0; q < S; ++q) {
+        const int ns = aseq[(size_t)l * S + q].nsplit;
+        for (int c = 0; c < hkv; ++c)
+          for (int sp = 0; sp < ns; ++sp, ++g) {
+            const int x = g % N_XCD;
+            for (int qb = 0; qb < qblocks[q]; ++qb)
+              work[nw + (off[x] + qb) * N_XCD + x] = make_int4(q, c, qb, sp);
+            off[x] += (size_t)qblocks[q];
+          }
+      }
+      nw += rounds * N_XCD;
       // drop the trailing empty entries of the last round
       while (nw > (size_t)work_off[l] && work[nw - 1].x < 0) --nw;
       work_cnt[l] = (int)nw - work_off[l];
