@@ -767,7 +767,6 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     if (rc) return rc;
     p.prefix.resize(L2);
     p.src = m->plan_src.data() + (size_t)q * L2;
-    for (int i = 0; i < L2; ++i) p.src[i].clear();
     // states per budget before item i (distinct subsets of that weight, capped at the beam;
     // 0/1 = reachability for the one-state DP)
     std::vector<int> cnt(B, 0), nxt(B);
@@ -777,9 +776,19 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       const int w = p.w[i];
       pre += w;
       p.prefix[i] = pre;
+      // slot j of budget s is a source iff j < cnt[s]; written without branches (an entry is
+      // kept by advancing past it), since reachability is irregular
+      std::vector<int32_t>& src = p.src[i];
+      src.resize((size_t)B * K);
+      int n = 0;
       for (int s = 0; s + w <= B - 1; ++s)
-        for (int j = 0; j < cnt[s]; ++j) p.src[i].push_back(s * Kb + j);
-      for (int b = 0; b < B; ++b) nxt[b] = std::min(K, cnt[b] + (b >= w ? cnt[b - w] : 0));
+        for (int j = 0; j < K; ++j) {
+          src[n] = s * Kb + j;
+          n += j < cnt[s];
+        }
+      src.resize(n);
+      for (int b = 0; b < std::min(w, B); ++b) nxt[b] = cnt[b];
+      for (int b = w; b < B; ++b) nxt[b] = std::min(K, cnt[b] + cnt[b - w]);
       cnt.swap(nxt);
     }
   }
@@ -1337,9 +1346,10 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       std::memcpy(res->masks + dst * mw, hmask + src * mw, (size_t)mw * 8);
       res->cos[dst] = hvalid[src] ? hcos[(size_t)q * Bm + b] : std::numeric_limits<float>::quiet_NaN();
       res->valid[dst] = hvalid[src];
-      double td = fixed;
-      for (int i = 0; i < L2; ++i)
-        if ((hmask[src * mw + i / 64] >> (i % 64)) & 1ull) td += p.t[i];
+      double td = fixed;  // executed items' latencies in item order
+      for (int wd = 0; wd < mw; ++wd)
+        for (uint64_t bits = hmask[src * mw + wd]; bits; bits &= bits - 1)
+          td += p.t[wd * 64 + __builtin_ctzll(bits)];
       res->t_draft[dst] = td;
     }
     for (int i = 0; i < L2; ++i) res->item_weight[(size_t)q * L2 + i] = p.w[i];

@@ -234,6 +234,17 @@ class Result:
         return self.tokens_flat[off:off + (B + 1) * w].reshape(B + 1, w)
 
 
+class PreparedSeqs:
+    """A knapspec_seq array (device pointers, context lengths, windows) built from a list of
+    sequence dicts; keeps the ctypes arrays alive."""
+
+    def __init__(self, model: "Model", seqs: List[dict]):
+        self.carr, self._keep = model._seq_array(seqs)
+        self.n = len(seqs)
+        self.windows = [int(sq.get("window", 1)) for sq in seqs]
+        self._tensors = seqs  # the tensors whose pointers the array holds
+
+
 class Model:
     """Owns a knapspec_model handle built from torch device tensors (kept alive here)."""
 
@@ -273,24 +284,29 @@ class Model:
                                    int(sq.get("window", 1)))
         return carr, keep
 
-    def solve(self, seqs: List[dict], n_budgets: int, gamma, tau: float = -math.inf,
+    def prepare(self, seqs: List[dict]) -> "PreparedSeqs":
+        """The knapspec_seq array of ``seqs`` built once, for repeated solves over the same
+        tensors (the pointers are read now; the tensors' contents may change between solves)."""
+        return PreparedSeqs(self, seqs)
+
+    def solve(self, seqs, n_budgets: int, gamma, tau: float = -math.inf,
               max_skip_weight: int = -1, flags: int = 0, stream=None,
               result: Optional[Result] = None, beam: int = 1,
               static_scratch: bool = False) -> Result:
         """seqs: dicts with ctx (int), k_cache / v_cache (lists of device tensors per layer,
         [hkv][capacity][dh]), x0 (device float32 [window][d] or [d]) and optionally window
-        (int, default 1).  static_scratch: call knapspec_solve_static (per-solve device
-        buffers in the library's static scratch; allocates nothing)."""
+        (int, default 1); or a PreparedSeqs of such a list.  static_scratch: call
+        knapspec_solve_static (per-solve device buffers in the library's static scratch;
+        allocates nothing)."""
         torch = self._torch
-        S = len(seqs)
-        carr, keep = self._seq_array(seqs)
+        prep = seqs if isinstance(seqs, PreparedSeqs) else PreparedSeqs(self, seqs)
+        S = prep.n
         s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
-        args = knapspec_solve_args(S, carr, int(n_budgets), int(gamma[0]), int(gamma[1]),
+        args = knapspec_solve_args(S, prep.carr, int(n_budgets), int(gamma[0]), int(gamma[1]),
                                    float(tau), int(max_skip_weight), int(flags), C.c_void_p(s),
                                    int(beam))
         res = result if result is not None else Result(
-            S, n_budgets, 2 * self.n_layers, self.mw, flags,
-            windows=[int(sq.get("window", 1)) for sq in seqs])
+            S, n_budgets, 2 * self.n_layers, self.mw, flags, windows=prep.windows)
         fn, name = ((knapspec_solve_static, "knapspec_solve_static") if static_scratch
                     else (knapspec_solve, "knapspec_solve"))
         _check(fn(self.handle, C.byref(args), C.byref(res.struct)), name)

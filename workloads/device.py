@@ -77,6 +77,7 @@ class DeviceProblem:
                     max_ctx=max(self.caps), max_window=self.window, max_beam=max_beam)
         torch.cuda.synchronize()
         self.model = ks.Model(desc, self.layers)
+        self._prepared = {}
         lat = wl.latency
         self.model.set_latency(lat.attn_base, lat.attn_per_token, lat.mlp, lat.fixed)
         # LM head of the acceptance estimate: host copy (widened) for the oracle, device copy
@@ -110,9 +111,14 @@ class DeviceProblem:
     def solve(self, n_budgets=None, gamma=None, tau=-math.inf, max_skip_weight=-1, flags=0,
               ctxs=None, result=None, resolve=None, beam=1):
         wl = self.wl
-        return self.model.solve(self.seq_args(ctxs, resolve), n_budgets or wl.n_budgets,
-                                gamma or wl.gamma, tau, max_skip_weight, flags, result=result,
-                                beam=beam)
+        # the knapspec_seq array of a (contexts, re-solve) pair is built once: the tensors
+        # behind it stay in place (set_x0 copies into them)
+        key = (tuple(ctxs) if ctxs is not None else None, resolve)
+        prep = self._prepared.get(key)
+        if prep is None:
+            prep = self._prepared[key] = self.model.prepare(self.seq_args(ctxs, resolve))
+        return self.model.solve(prep, n_budgets or wl.n_budgets, gamma or wl.gamma, tau,
+                                max_skip_weight, flags, result=result, beam=beam)
 
     def close(self):
         self.model.close()
