@@ -6,7 +6,7 @@ leave the GEMMs, the attention and its partial results.
   live rows are every reachable row, in the host planner's order, and the attention splits are
   the host planner's, so the results are bit-identical to those of the solve that keeps the
   rows planned from reachability (KNAPSPEC_KEEP_PRUNED_ROWS) -- one and several sequences,
-  float32 and bfloat16, windows of 1 and 3 tokens.
+  float32 and bfloat16, windows of 1, 2 and 3 tokens, with and without the LM-head estimate.
 * Everything pruned after the first item (tau = 1.5): only the reference rows stay; results
   are bit-identical too (all budgets invalid).
 * Pruned for real (tau = 0.5, a skip cap): both plans pass parity against the oracle's DP
@@ -38,20 +38,22 @@ def _same(a, b, what):
         assert np.array_equal(a, b), what
 
 
-def _bit_equal(wl, ctxs, tau=-math.inf, cap=-1, window=1, n_budgets=None, seed=0):
+def _bit_equal(wl, ctxs, tau=-math.inf, cap=-1, window=1, n_budgets=None, seed=0, lm_vocab=0):
     from workloads.device import DeviceProblem
 
     print(f"\n[case] live rows vs kept rows {wl.name} ctxs={ctxs} tau={tau} cap={cap} "
-          f"window={window} B={n_budgets or wl.n_budgets}", flush=True)
+          f"window={window} B={n_budgets or wl.n_budgets} vocab={lm_vocab}", flush=True)
     prob = DeviceProblem(wl, seed, ctxs=ctxs, window=window,
-                         max_budgets=n_budgets or wl.n_budgets)
+                         max_budgets=n_budgets or wl.n_budgets, lm_vocab=lm_vocab)
     B = n_budgets or wl.n_budgets
     flags = 3 if window == 1 else 0
+    if lm_vocab:
+        flags |= prob.ks.KNAPSPEC_ALPHA_LM_HEAD
     live = prob.solve(n_budgets=B, tau=tau, max_skip_weight=cap, flags=flags)
     kept = prob.solve(n_budgets=B, tau=tau, max_skip_weight=cap, flags=flags | KEEP)
     again = prob.solve(n_budgets=B, tau=tau, max_skip_weight=cap, flags=flags)
     for name in ("masks", "cos", "valid", "t_draft", "item_weight", "best_budget",
-                 "best_gamma", "best_tpt", "decisions", "margins", "alpha"):
+                 "best_gamma", "best_tpt", "decisions", "margins", "alpha", "tokens_flat"):
         _same(getattr(live, name), getattr(kept, name), name)
         _same(getattr(live, name), getattr(again, name), name + " (repeat)")
     n_valid = int(live.valid.sum())
@@ -76,6 +78,11 @@ def test_nothing_pruned_bf16_three_sequences():
 
 def test_nothing_pruned_window3_skip_cap():
     _bit_equal(WORKLOADS["tiny"], [100, 40], cap=10 ** 6, window=3)
+
+
+def test_nothing_pruned_window_lm_head():
+    # the last item's select feeds the LM-head rows at their planned places either way
+    _bit_equal(WORKLOADS["tiny"], [130, 60], cap=10 ** 6, window=2, lm_vocab=512)
 
 
 def test_nothing_pruned_mlp_items_planned_too():

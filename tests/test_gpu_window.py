@@ -30,7 +30,8 @@ BETA = {"f32": 1e-5, "bf16": 2e-3}
 LM_BAND = {"f32": 1e-3, "bf16": 0.05}
 
 
-def run_window(wl, r, ctx, n_budgets=None, lm_vocab=0, max_window=None, seed=0):
+def run_window(wl, r, ctx, n_budgets=None, lm_vocab=0, max_window=None, seed=0,
+               tau=-math.inf):
     from workloads.device import DeviceProblem
 
     B = n_budgets or wl.n_budgets
@@ -45,7 +46,7 @@ def run_window(wl, r, ctx, n_budgets=None, lm_vocab=0, max_window=None, seed=0):
         prob.host_x0[0] = x
         prob.x0[0] = prob.torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
     flags = 3 | (prob.ks.KNAPSPEC_ALPHA_LM_HEAD if lm_vocab else 0)
-    res = prob.solve(n_budgets=B, flags=flags)
+    res = prob.solve(n_budgets=B, flags=flags, tau=tau)
     beta = BETA[wl.shape.dtype]
     n_items = 2 * wl.shape.n_layers
     lat = {"attn_base": wl.latency.attn_base, "attn_per_token": wl.latency.attn_per_token,
@@ -53,8 +54,8 @@ def run_window(wl, r, ctx, n_budgets=None, lm_vocab=0, max_window=None, seed=0):
     items = ko.DecoderItems(decoder_shape(wl), prob.host_layers, prob.host_kv[0], ctx,
                             cache_widened=True)
     x0 = prob.host_x0[0]
-    orc = ko.solve(decoder_shape(wl), None, None, x0, ctx, lat, B, wl.gamma, apply_item=items,
-                   w_lm=prob.host_lm if lm_vocab else None)
+    orc = ko.solve(decoder_shape(wl), None, None, x0, ctx, lat, B, wl.gamma, tau=tau,
+                   apply_item=items, w_lm=prob.host_lm if lm_vocab else None)
     rep = compare(orc, res, 0, beta, items, x0, wl.gamma, n_items)
     print(f"  {rep.line()}", flush=True)
     assert rep.mismatched_clean == 0
@@ -105,6 +106,15 @@ def test_tiny_f32_window_lm_head_alpha():
     assert np.array_equal(res.masks[0], orc.masks)
     assert np.allclose(res.alpha[0].astype(np.float64), orc.alpha, rtol=0, atol=1e-6)
     assert (int(res.best_budget[0]), int(res.best_gamma[0])) == (orc.best_budget, orc.best_gamma)
+
+
+def test_tiny_f32_window_lm_head_alpha_pruned():
+    # tau pruning on: the live-row plan drops pruned budgets from every item after the first,
+    # while the last item's rows still feed the LM-head pass at their planned places
+    res, orc, rep = run_window(WORKLOADS["tiny"], 3, ctx=130, lm_vocab=512, tau=0.3)
+    assert np.array_equal(res.masks[0], orc.masks)
+    assert np.array_equal(res.valid[0].astype(bool), orc.dp.valid)
+    assert np.allclose(res.alpha[0].astype(np.float64), orc.alpha, rtol=0, atol=1e-6)
 
 
 def test_bf16_window_lm_head_alpha():
