@@ -3,11 +3,12 @@
 // pruning the DP's candidate states cuts its memory and optimisation work) also leave the
 // item's GEMM rows, attention query blocks and partial results.
 //
-// One workgroup of 1024 threads (thread b = budget b):
-//   1. per sequence, a block-wide prefix count over the live candidate sources (valid flag set
-//      and b + w_i <= B - 1) gives each live source its compacted row; the maps of the item
-//      (activation row, sequence, window token, state slot, execute row of the target budget)
-//      are rewritten, the reference follows the sequence's live sources;
+// One workgroup of 1024 threads:
+//   1. a prefix count over each sequence's live candidate sources (valid flag set and
+//      b + w_i <= B - 1) gives each live source its row -- block-wide with one budget per
+//      thread for a single sequence, else one wave per sequence (16 at a time); the maps of
+//      the item (activation row, sequence, window token, state slot, execute row of the target
+//      budget) are rewritten, the reference follows the sequence's live sources;
 //   2. attention items: each sequence's context split count for its live rows, by the cost
 //      model of the host planner (fewest dispatch rounds x (tiles per workgroup + fixed cost),
 //      ties to fewer workgroups, then to the earlier candidate), every candidate evaluated by a
@@ -48,7 +49,6 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
     base += w < wave ? s : 0;
     tot += s;
   }
-  lds_sync();  // s_wave is reused by the next scan
   *total = tot;
   return base + x - v;
 }
@@ -70,6 +70,24 @@ __device__ unsigned long long block_min_u64(unsigned long long v, unsigned long 
   return m;
 }
 
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// exclusive prefix sum of v over the wave's lanes
+__device__ __forceinline__ int wave_excl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+
 // number of i in [0, n) with i % 8 == x
 __device__ __forceinline__ int count_mod8(int n, int x) { return n > x ? (n - x + 7) / 8 : 0; }
 
@@ -82,57 +100,123 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
   __shared__ int s_qb[COMPACT_MAX_SEQS], s_tiles[COMPACT_MAX_SEQS], s_ns[COMPACT_MAX_SEQS];
   __shared__ int s_gp[COMPACT_MAX_SEQS + 1];
   __shared__ int s_load[8];
+  __shared__ int s_R;
   const int tid = threadIdx.x;
   const int S = a.n_seqs;
   // the layer's context lengths, loaded with the first sequence's inputs
   const int ctx_t = (a.aseq && tid < S) ? a.aseq[tid].ctx : 0;
 
-  // ---- 1. rows
-  int row_off = 0;
-  for (int q = 0; q < S; ++q) {
-    const int w = a.info[q].w, wr = a.info[q].win;
-    const int next_ref = a.prev_info[q].next_ref_row;
+  // ---- 1. rows.  One wave per sequence (sequences in parallel); lane l holds the contiguous
+  //      budgets [l*per, (l+1)*per), so a wave-wide exclusive prefix of the lanes' live counts
+  //      plus the count within the lane is a source's rank in budget order.
+  const int wave = tid >> 6, lane = tid & 63;
+  if (S == 1) {
+    // one sequence: thread b holds budget b, a block-wide prefix count gives the ranks
+    const int w = a.info[0].w, wr = a.info[0].win;
+    const int next_ref = a.prev_info[0].next_ref_row;
     const int b = tid;
-    const size_t qb = (size_t)q * a.Bm + b;
-    // loads of every budget of the sequence (in range for b < B), independent of w
-    const bool inb = b < a.B;
-    const int vflag = inb ? a.valid[qb * a.kmax] : 0;
-    const int prow = inb ? a.prev_next_row[qb * a.kmax] : 0;
+    const bool inb = b < a.B;  // loads independent of w, issued together
+    const int vflag = inb ? a.valid[(size_t)b * a.kmax] : 0;
+    const int prow = inb ? a.prev_next_row[(size_t)b * a.kmax] : 0;
     const bool cand = inb && b + w <= a.B - 1;
     const bool live = cand && vflag != 0;
     int nlive;
     const int rank = block_excl_scan(live ? 1 : 0, s_wave, &nlive);
-    const size_t st_q = (size_t)q * (a.Bm + 1) * a.kmax;  // first state slot of the sequence
     if (cand) {
-      const int row = row_off + rank * wr;
-      a.exec_row[(qb + w) * a.kmax] = live ? row : -1;
-      if (live) {
+      const int row = rank * wr;
+      a.exec_row[(size_t)(b + w) * a.kmax] = live ? row : -1;
+      if (live)
+        for (int t = 0; t < wr; ++t) {
+          a.amap[row + t] = prow + t;
+          a.row_seq[row + t] = 0;
+          a.row_tok[row + t] = t;
+          a.row_state[row + t] = (int)((size_t)b * a.kmax * a.wmax + t);
+        }
+    }
+    const int ref = nlive * wr;
+    if (tid < wr) {
+      a.amap[ref + tid] = next_ref + tid;
+      a.row_seq[ref + tid] = 0;
+      a.row_tok[ref + tid] = tid;
+      a.row_state[ref + tid] = (int)((size_t)a.Bm * a.kmax * a.wmax + tid);
+    }
+    if (tid == 0) {
+      a.info[0].row_off = 0;
+      a.info[0].M = (nlive + 1) * wr;
+      a.info[0].ref_row = ref;
+      s_M[0] = (nlive + 1) * wr;
+      s_off[0] = 0;
+      s_R = (nlive + 1) * wr;
+    }
+    lds_sync();
+  } else {
+    // several sequences: one wave per sequence; lane l holds the contiguous budgets
+    // [l*per, (l+1)*per), so a wave-wide exclusive prefix of the lanes' live counts plus the
+    // count within the lane is a source's rank in budget order
+    const int per = (a.B + 63) / 64;
+    for (int q = wave; q < S; q += CW) {  // pass A: live sources of each sequence
+      const int w = a.info[q].w, wr = a.info[q].win;
+      int n = 0;
+      for (int k = 0; k < per; ++k) {
+        const int b = lane * per + k;
+        if (b < a.B && b + w <= a.B - 1 && a.valid[((size_t)q * a.Bm + b) * a.kmax]) ++n;
+      }
+      const int total = wave_sum(n);
+      if (lane == 0) s_M[q] = (total + 1) * wr;
+    }
+    lds_sync();
+    if (tid == 0) {
+      int r = 0;
+      for (int q = 0; q < S; ++q) {
+        s_off[q] = r;
+        r += s_M[q];
+      }
+      s_R = r;
+    }
+    lds_sync();
+    for (int q = wave; q < S; q += CW) {  // pass B: maps
+      const int w = a.info[q].w, wr = a.info[q].win;
+      const int next_ref = a.prev_info[q].next_ref_row;
+      const int row_off = s_off[q];
+      const size_t st_q = (size_t)q * (a.Bm + 1) * a.kmax;  // first state slot of the sequence
+      int n = 0;
+      for (int k = 0; k < per; ++k) {
+        const int b = lane * per + k;
+        if (b < a.B && b + w <= a.B - 1 && a.valid[((size_t)q * a.Bm + b) * a.kmax]) ++n;
+      }
+      int rank = wave_excl_scan(n);
+      for (int k = 0; k < per; ++k) {
+        const int b = lane * per + k;
+        if (!(b < a.B && b + w <= a.B - 1)) continue;
+        const size_t qb = (size_t)q * a.Bm + b;
+        const bool live = a.valid[qb * a.kmax] != 0;
+        const int row = row_off + rank * wr;
+        a.exec_row[(qb + w) * a.kmax] = live ? row : -1;
+        if (!live) continue;
+        const int prow = a.prev_next_row[qb * a.kmax];
         for (int t = 0; t < wr; ++t) {
           a.amap[row + t] = prow + t;
           a.row_seq[row + t] = q;
           a.row_tok[row + t] = t;
           a.row_state[row + t] = (int)((st_q + (size_t)b * a.kmax) * a.wmax + t);
         }
+        ++rank;
+      }
+      const int ref = row_off + s_M[q] - wr;
+      if (lane < wr) {
+        a.amap[ref + lane] = next_ref + lane;
+        a.row_seq[ref + lane] = q;
+        a.row_tok[ref + lane] = lane;
+        a.row_state[ref + lane] = (int)((st_q + (size_t)a.Bm * a.kmax) * a.wmax + lane);
+      }
+      if (lane == 0) {
+        a.info[q].row_off = row_off;
+        a.info[q].M = s_M[q];
+        a.info[q].ref_row = ref;
       }
     }
-    const int ref = row_off + nlive * wr;
-    if (tid < wr) {
-      a.amap[ref + tid] = next_ref + tid;
-      a.row_seq[ref + tid] = q;
-      a.row_tok[ref + tid] = tid;
-      a.row_state[ref + tid] = (int)((st_q + (size_t)a.Bm * a.kmax) * a.wmax + tid);
-    }
-    const int M = (nlive + 1) * wr;
-    if (tid == 0) {
-      a.info[q].row_off = row_off;
-      a.info[q].M = M;
-      a.info[q].ref_row = ref;
-      s_M[q] = M;
-      s_off[q] = row_off;
-    }
-    row_off += M;
   }
-  const int R = row_off;
+  const int R = s_R;
   for (int c = R + tid; c < a.R_plan; c += COMPACT_THREADS) {
     a.amap[c] = 0;
     a.row_seq[c] = 0;
@@ -144,7 +228,6 @@ __global__ __launch_bounds__(COMPACT_THREADS) void compact_kernel(CompactArgs a)
 
   // ---- 2. context splits of the live rows
   const int G = a.hq / a.hkv;
-  lds_sync();  // s_M, s_off
   if (tid < S) {
     s_qb[tid] = ceil_div(G * s_M[tid], a.qb_rows);
     s_tiles[tid] = ceil_div(ctx_t, 64);

@@ -179,7 +179,7 @@ struct SelectArgs {
 // planner's cost model: fewest rounds x (tiles + fixed cost), ties to fewer workgroups, then
 // to the earlier candidate) and writes the layer's work list, groups of query blocks dealt to
 // the dies round-robin.
-constexpr int COMPACT_THREADS = 1024;   // one budget per thread: n_budgets <= 1024
+constexpr int COMPACT_THREADS = 1024;   // 16 waves, one sequence each; n_budgets <= 1024
 constexpr int COMPACT_MAX_SEQS = 64;
 
 struct CompactArgs {

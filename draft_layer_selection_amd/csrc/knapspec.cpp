@@ -83,7 +83,7 @@ MapLayout map_layout(int L2, int n_layers, size_t S, size_t Bm, size_t Rmax, int
   // per layer: every (sequence, KV head, query block, split) once, plus the empty entries
   // that keep each die's share of the list aligned (at most one query-block group per die)
   const size_t qb_max = (G * (Bm + 1) * wmax * kmax + 63) / 64;
-  L.max_work = (size_t)n_layers * (S * hkv * qb_max * asplit_max + N_XCD * qb_max);
+  L.max_work = (size_t)n_layers * (S * hkv * qb_max * asplit_max + N_XCD * (S * qb_max + 1));
   L.work = c.take(L.max_work * 16);
   L.amap = c.take((size_t)L2 * Rmax * 4);
   L.rlive = c.take((size_t)L2 * 4);
@@ -918,17 +918,21 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       if (part > m->part_slots)
         return fail(KNAPSPEC_EINVAL, "internal: attention partial slots overflow");
       if (compact && l > 0) {
-        // the live-row plan writes this layer's list on the device: reserve room for any
-        // split choice it may make (at most the larger of one dispatch round and the
-        // unsplit pairs, plus the die round-robin's padding) -- placed after the host lists
-        size_t need = 0, qbs = 0;
+        // the live-row plan writes this layer's list on the device, placed after the host
+        // lists.  Its split choice is limited to lists that fit the room reserved here: the
+        // unsplit pairs (always), this plan's own list (what the live plan picks when nothing
+        // is pruned) and half as much again (fewer live rows favour more splits), each plus
+        // the die round-robin's padding; the launch covers the whole room (empty entries exit)
+        size_t need = 0, qbs = 0, planned = 0;
         for (int q = 0; q < S; ++q) {
           if (tiles[q] > 0) need += (size_t)pairs[q];
           qbs += (size_t)qblocks[q];
+          planned += (size_t)pairs[q] * (size_t)aseq[(size_t)l * S + q].nsplit;
         }
         const size_t pad = 8 * (qbs + 1);
         const size_t bound = max_work / (size_t)d.n_layers;
-        work_cnt[l] = (int)std::max(need + pad, std::min(std::max(need, (size_t)slots) + pad, bound));
+        const size_t want = std::max(planned, (size_t)slots) * 3 / 2 + pad;
+        work_cnt[l] = (int)std::max({need + pad, planned + pad, std::min(want, bound)});
         continue;
       }
       work_off[l] = (int)nw;

@@ -211,6 +211,9 @@ def main(argv=None):
                     help="only run N solves at each tau of --taus (e.g. under a kernel tracer)")
     ap.add_argument("--kept-rows", action="store_true",
                     help="with --solves: keep the pruned budgets' rows (KNAPSPEC_KEEP_PRUNED_ROWS)")
+    ap.add_argument("--batch", action="store_true",
+                    help="with --solves: solve all of the preset's sequences together at their "
+                         "own contexts (e.g. the 16-sequence preset) instead of one at --ctx")
     args = ap.parse_args(argv)
 
     from .device import DeviceProblem
@@ -222,8 +225,11 @@ def main(argv=None):
     taus = [float(x) for x in args.taus.split(",")]
     cap = max(max(ctx_list), wl.ctx) + 16  # room for a draft/verify block past the context
     beams = [int(x) for x in args.beams.split(",")] if args.beams else []
-    prob = DeviceProblem(wl, args.seed, ctxs=[wl.ctx], caps=[cap],
-                         max_beam=max(beams) if beams else 1, lm_vocab=args.draft_verify)
+    if args.solves and args.batch:
+        prob = DeviceProblem(wl, args.seed)
+    else:
+        prob = DeviceProblem(wl, args.seed, ctxs=[wl.ctx], caps=[cap],
+                             max_beam=max(beams) if beams else 1, lm_vocab=args.draft_verify)
     if args.solves:
         import torch
 
@@ -232,8 +238,9 @@ def main(argv=None):
             for k in range(args.solves):
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
-                prob.solve(tau=tau, flags=flags)
-                print(f"tau {tau} solve {k}: {1e3 * (time.perf_counter() - t0):.3f} ms",
+                res = prob.solve(tau=tau, flags=flags)
+                print(f"tau {tau} solve {k}: {1e3 * (time.perf_counter() - t0):.3f} ms, "
+                      f"valid budgets {int(res.valid.sum())} over {len(prob.ctxs)} sequences",
                       flush=True)
         prob.close()
         return
