@@ -54,7 +54,7 @@ extern "C" {
 #define KNAPSPEC_RETURN_DECISIONS 1 /* fill knapspec_result.decisions */
 #define KNAPSPEC_RETURN_MARGINS 2   /* fill knapspec_result.margins */
 #define KNAPSPEC_ALPHA_LM_HEAD 4    /* TPT acceptance from the LM head (knapspec_set_lm_head) */
-#define KNAPSPEC_KEEP_PRUNED_ROWS 8 /* keep the rows of pruned budgets (see knapspec_solve) */
+#define KNAPSPEC_KEEP_PRUNED_ROWS 8 /* keep pruned budgets' rows (see knapspec_solve) */
 
 #define KNAPSPEC_WINDOW_MAX 16 /* largest r of an r-token window */
 #define KNAPSPEC_BEAM_MAX 8   /* largest beam width of the beam variant of the DP */
@@ -176,6 +176,13 @@ typedef struct {
  * streams each layer's KV cache once per sequence for all rows, and the per-budget
  * cosine/select.  Enqueues on args->hip_stream, synchronises once, copies the per-budget
  * results to `result` and runs the TPT grid on the host with a = clamp(cos, 0, 1).
+ * Rows are planned from budget reachability.  With tau or the skip cap on (one-state DP, up to
+ * 64 sequences) the rows of every item after the first are rebuilt on the device from the
+ * previous item's valid flags, so budgets pruned so far leave the attention (and, above 512
+ * rows, the MLP GEMMs) -- review, Figure 4 caption: pruning cuts the optimisation work.
+ * KNAPSPEC_KEEP_PRUNED_ROWS keeps the reachability plan instead (results agree within
+ * floating-point reordering of the attention's context splits; bit-identical when nothing is
+ * pruned).
  * The acceptance proxy a = clamp(cos) stands in for the paper's history estimate (Eq. 9),
  * which the pages do not print.  With KNAPSPEC_ALPHA_LM_HEAD (needs knapspec_set_lm_head)
  * the grid instead uses, per budget, the fraction of the window's tokens whose greedy token
@@ -197,7 +204,9 @@ int knapspec_solve(knapspec_model* model, const knapspec_solve_args* args,
  * max_budgets, max_seqs, max_ctx, max_window, max_beam and the decoder shape) exceed 64 MiB --
  * e.g. a 28-layer, d 2048 decoder loaded for 128 budgets fits, a Llama-3-8B shape for 256
  * budgets does not -- or when profiling is enabled.  Nothing in the array needs to start at
- * zero: every buffer a solve reads is written earlier in the same solve.  All calls on one GPU
+ * zero: every value a solve uses is written earlier in the same solve (launch rows past the
+ * live rows of a pruned solve may compute on an earlier call's data; nothing reads their
+ * results).  All calls on one GPU
  * share the array: calls that overlap on one GPU (several threads, streams or models) race
  * and must be serialised by the caller. */
 int knapspec_solve_static(knapspec_model* model, const knapspec_solve_args* args,
