@@ -95,6 +95,22 @@ def test_pruned_parity_mlp_items_planned_too():
     run_case(WORKLOADS["tiny"], ctxs=[256, 100, 31, 0], tau=0.3, n_budgets=200)
 
 
+def test_nothing_pruned_twenty_sequences():
+    # more sequences than the plan kernel has waves: each wave plans several sequences
+    ctxs = [(37 * k) % 251 for k in range(20)]
+    _bit_equal(WORKLOADS["tiny"], ctxs, tau=-2.0, n_budgets=40)
+
+
+def test_pruned_parity_twenty_sequences():
+    run_case(WORKLOADS["tiny"], ctxs=[(37 * k) % 251 for k in range(20)], tau=0.3, n_budgets=40)
+
+
+def test_pruned_parity_1024_budgets():
+    # the largest budget count: the single-sequence plan holds one budget per thread
+    wl = scaled(WORKLOADS["tiny"], n_layers=4, name="tiny_l4_b1024")
+    run_case(wl, ctxs=[130], tau=0.3, n_budgets=1024)
+
+
 def test_everything_pruned_after_first_item():
     res = _bit_equal(_bf16_gqa(), [200, 90], tau=1.5, n_budgets=24)
     assert res.valid.sum() == 0
