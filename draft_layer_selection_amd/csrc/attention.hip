@@ -141,8 +141,9 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// MFMA attention partial (bf16, dh = 128): 8 waves x 32 query rows = 256 query rows per
-// workgroup (one workgroup per CU), 64-key tiles.
+// MFMA attention partial (bf16, dh = 128 or 64): 8 waves x 32 query rows = 256 query rows per
+// workgroup (one workgroup per CU), 64-key tiles.  The layout notes below are for dh = 128;
+// AttnGeom states the dh = 64 swizzles.
 //   * K and V tiles are loaded with range-checked 16-byte buffer loads into registers one
 //     iteration ahead and stored to a K ring and a V ring of four slots each, both kept as
 //     [key][dh] (measured faster than loading global -> LDS directly, which competes with the
@@ -163,11 +164,9 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 //     ALU busy at once.  K of tile t is read in iteration t-1 and V in iteration t; tile t is
 //     loaded in iteration t-3 and stored to LDS in iteration t-2.
 // ------------------------------------------------------------------------------------
-constexpr int DHM = 128;
 constexpr int KT = 64;                 // keys per tile
 constexpr int QB = 256;                // query rows per workgroup
 constexpr int NR = 4;                  // slots of the K ring and of the V ring
-constexpr int TILE_BYTES = KT * DHM * 2;
 constexpr float RESCALE_LOG2 = 8.f;    // allowed growth of p above 1 before rescaling
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -201,7 +200,28 @@ __device__ __forceinline__ void attn_wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// Head sizes 128 and 64.  A key's row of K or V is ROWB = 2*DH bytes: 16 chunks of 16 bytes at
+// DH = 128, 8 at DH = 64; the swizzles below keep both the 16-byte K reads and the transposing
+// V reads conflict-free (16 consecutive keys, resp. the 32 lanes of a read phase, on distinct
+// 16-byte slots modulo 256 bytes).
+template <int DH>
+struct AttnGeom {
+  static constexpr int ROWB = 2 * DH;
+  static constexpr int TB = KT * ROWB;            // bytes of one K (or V) tile
+  static constexpr int CPW = TB / 1024 / 8;       // 1 KB load chunks per wave per tile
+  static constexpr int LPR = ROWB / 16;           // lanes per key row in a load chunk
+  static constexpr int KSTEPS = DH / 16;          // 16-wide steps of q . k
+  static constexpr int DB = DH / 32;              // 32-row dh blocks of O^T
+  // slot of 16-byte chunk c of key k: K read by 16 consecutive keys, V by the transposing read
+  static __device__ __forceinline__ int swz_k(int k) { return DH == 128 ? (k & 15) : ((k >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int k) { return DH == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+};
+
+template <int DH>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
+  using Geo = AttnGeom<DH>;
+  constexpr int ROWB = Geo::ROWB, TILE_BYTES = Geo::TB, CPW = Geo::CPW, LPR = Geo::LPR;
+  constexpr int KSTEPS = Geo::KSTEPS, DB = Geo::DB;
   const int4 wk = a.work[blockIdx.x];
   if (wk.x < 0) return;
   const AttnSeq S = a.seqs[wk.x];
@@ -225,79 +245,80 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const float cs = a.scale_log2;
 
   // this lane's query row as the B operand of S^T = K Q^T: 8 K-steps of 16 dh
-  const bf16* qp = (const bf16*)a.Q + ((size_t)row * a.hq + h) * DHM + hi * 8;
-  bf16x8 qf[8];
+  const bf16* qp = (const bf16*)a.Q + ((size_t)row * a.hq + h) * DH + hi * 8;
+  bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
+  for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
 
   __shared__ __attribute__((aligned(1024))) unsigned char kring[NR][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char vring[NR][TILE_BYTES];
 
-  // Loads: a tile is 16 chunks of 4 keys of K and 16 of V; wave w moves chunks w and w + 8
-  // of each.  Lane -> key 4*chunk + lane/16 of the tile, LDS slot lane%16 <- global 16-byte
-  // chunk slot ^ swz(key), swz = key & 15 for K and 4*(key & 3) for V.  The loads are
-  // range-checked buffer loads whose resource starts at the tile's first key and ends at the
-  // sequence's last cached key: keys past the cache read as zeros (their scores are masked),
-  // and the per-lane byte offsets stay the same for every tile.
-  int kvo[2], vvo[2];
+  // Loads: a tile is TB/1024 chunks of 1 KB (1024/ROWB keys each) of K and as many of V;
+  // wave w moves chunks w, w + 8, ... of each.  Lane -> key (1024/ROWB)*chunk + lane/LPR of the
+  // tile, LDS slot lane%LPR <- global 16-byte chunk slot ^ swz(key) (swz_k for K, swz_v for
+  // V).  The loads are range-checked buffer loads whose resource starts at the tile's first key
+  // and ends at the sequence's last cached key: keys past the cache read as zeros (their
+  // scores are masked), and the per-lane byte offsets stay the same for every tile.
+  int kvo[CPW], vvo[CPW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int kk = 4 * (wave + 8 * j) + (lane >> 4);
-    kvo[j] = kk * 256 + 16 * ((lane & 15) ^ (kk & 15));
-    vvo[j] = kk * 256 + 16 * ((lane & 15) ^ (4 * (kk & 3)));
+  for (int j = 0; j < CPW; ++j) {
+    const int kk = (1024 / ROWB) * (wave + 8 * j) + lane / LPR;
+    kvo[j] = kk * ROWB + 16 * ((lane % LPR) ^ Geo::swz_k(kk));
+    vvo[j] = kk * ROWB + 16 * ((lane % LPR) ^ Geo::swz_v(kk));
   }
-  const char* khead = (const char*)S.k + (size_t)c * S.cap * DHM * 2;
-  const char* vhead = (const char*)S.v + (size_t)c * S.cap * DHM * 2;
+  const char* khead = (const char*)S.k + (size_t)c * S.cap * ROWB;
+  const char* vhead = (const char*)S.v + (size_t)c * S.cap * ROWB;
   auto tile_rsrc = [&](const char* head, int tile) {
     const int key0 = k0 + tile * KT;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)key0 * DHM * 2), (short)0,
-                                             (S.ctx - key0) * DHM * 2, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)key0 * ROWB), (short)0,
+                                             (S.ctx - key0) * ROWB, 0x00020000);
   };
   // one tile is staged through registers: loaded in one iteration, stored to LDS in the next
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 stg[4];  // this lane's K (0, 1) and V (2, 3) chunks of the staged tile
+  u32x4 stg[2 * CPW];  // this lane's K (0 .. CPW-1) and V (CPW ..) chunks of the staged tile
   auto load_tile = [&](int tile) {
     if (tile >= ntiles) return;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(khead, tile);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vhead, tile);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < CPW; ++j) {
       stg[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, kvo[j], 0, 0);
-      stg[2 + j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vvo[j], 0, 0);
+      stg[CPW + j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vvo[j], 0, 0);
     }
   };
   auto store_tile = [&](int tile, int slot) {
     if (tile >= ntiles) return;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < CPW; ++j) {
       *(u32x4*)&kring[slot][(wave + 8 * j) * 1024 + lane * 16] = stg[j];
-      *(u32x4*)&vring[slot][(wave + 8 * j) * 1024 + lane * 16] = stg[2 + j];
+      *(u32x4*)&vring[slot][(wave + 8 * j) * 1024 + lane * 16] = stg[CPW + j];
     }
   };
 
-  f32x16 o[4];
+  f32x16 o[DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = -INFINITY, lsum = 0.f;  // m: reference max of raw scores, shared by lanes l, l^32
   const float thresh = RESCALE_LOG2 / cs;
 
   // Loop-invariant LDS byte offsets within a slot.  K read for K-step ks of key l32 (+32 per
-  // key block): chunk 2ks + hi in slot chunk ^ (key & 15).  V^T read (transposing) of lane
+  // key block): chunk 2ks + hi in slot chunk ^ swz_k(key).  V^T read (transposing) of lane
   // (g = lane/16, e = (lane/4)%4, q = lane%4) for dh block db: key 4*(g/2) + e (+ the key
-  // offset of the MFMA step, a multiple of 8), dh 32db + 16(g%2) + 4q, i.e. chunk
-  // 4db + 2(g%2) + q/2, half q%2, slot chunk ^ 4*(key & 3) = chunk ^ 4e.
-  int koff[8], voff[4];
+  // offset of the MFMA step, a multiple of 8, which leaves swz_v unchanged), dh
+  // 32db + 16(g%2) + 4q, i.e. chunk 4db + 2(g%2) + q/2, half q%2, slot chunk ^ swz_v(key).
+  int koff[KSTEPS], voff[DB];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = l32 * 256 + 16 * ((2 * ks + hi) ^ (l32 & 15));
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    koff[ks] = l32 * ROWB + 16 * ((2 * ks + hi) ^ Geo::swz_k(l32));
   {
     const int tg = lane >> 4, te = (lane >> 2) & 3, tq = lane & 3;
     const int key = 4 * (tg >> 1) + te;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < DB; ++db) {
       const int ch = 4 * db + 2 * (tg & 1) + (tq >> 1);
-      voff[db] = key * 256 + 16 * (ch ^ (4 * te)) + 8 * (tq & 1);
+      voff[db] = key * ROWB + 16 * (ch ^ Geo::swz_v(key)) + 8 * (tq & 1);
     }
   }
   bf16x2 ones2;
@@ -307,31 +328,32 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   // Per-lane LDS addresses of the V reads in slot 0 of the V ring.  The ring sits above
   // 64 KB, past the reach of the 16-bit instruction offset, so the ring base is folded into
   // the (opaque) register once and slot, key-group and half offsets stay immediates.
-  const lds_u8* vbase[4];
+  const lds_u8* vbase[DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < DB; ++db) {
     unsigned a32 = (unsigned)(size_t)(const lds_u8*)&vring[0][0] + (unsigned)voff[db];
     asm volatile("" : "+v"(a32));
     vbase[db] = (const lds_u8*)(size_t)a32;
   }
-  // P.V of group g (keys 16g .. 16g+15 of the tile) for the four 32-row dh blocks; J = slot
+  // P.V of group g (keys 16g .. 16g+15 of the tile) for the 32-row dh blocks; J = slot
   auto pv_group = [&](int J, int g, const bf16x8& pf) {
-    const int kofs = J * TILE_BYTES + ((g >> 1) * 32 + 16 * (g & 1)) * 256;
+    const int kofs = J * TILE_BYTES + ((g >> 1) * 32 + 16 * (g & 1)) * ROWB;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < DB; ++db) {
       const s16x4 lo = lds_read_tr16(vbase[db] + kofs);
-      const s16x4 hv = lds_read_tr16(vbase[db] + kofs + 8 * 256);
+      const s16x4 hv = lds_read_tr16(vbase[db] + kofs + 8 * ROWB);
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
     }
   };
-  // scores of K-steps 2g, 2g+1 for both 32-key blocks
+  // scores of the K-steps of group g (KSTEPS/4 of them) for both 32-key blocks
   auto qk_steps = [&](const unsigned char* kst, int g, f32x16 (&sc)[2]) {
+    constexpr int PER = KSTEPS / 4;
 #pragma unroll
-    for (int ks = 2 * g; ks < 2 * g + 2; ++ks)
+    for (int ks = PER * g; ks < PER * g + PER; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)(kst + koff[ks] + kb * 32 * 256);
+        const bf16x8 kf = *(const bf16x8*)(kst + koff[ks] + kb * 32 * ROWB);
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
       }
   };
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       const float corr = __builtin_amdgcn_exp2f((m - mn) * cs);
       lsum *= corr;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= corr;
       m = mn;
@@ -439,10 +461,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   lsum = pair_sum(lsum);
   if (!tvalid) return;
   const size_t slot = attn_slot(S, sp, tt / G, a.hq, h);
-  float* op = a.Opart + slot * DHM;
+  float* op = a.Opart + slot * DH;
   // O^T accumulator: lane holds dh = 32*db + 8*(r/4) + 4*hi + r%4 of query l32
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       f32x4 v;
@@ -565,9 +587,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float* kself, cons
 
 }  // namespace
 
-int attention_qblock(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? QB : 64; }
-// MFMA kernel: 128 KB of LDS rings -> one per CU; VALU kernel: 64 threads, <= 33 KB LDS
-int attention_wgs_per_cu(int act, int dh) { return (act == ACT_BF16 && dh == 128) ? 1 : 4; }
+// bfloat16 at head size 64 or 128 runs the MFMA kernel, everything else the VALU kernel
+static bool mfma_path(int act, int dh) { return act == ACT_BF16 && (dh == 128 || dh == 64); }
+int attention_qblock(int act, int dh) { return mfma_path(act, dh) ? QB : 64; }
+// MFMA kernel: 64 KB (DH 64) or 128 KB (DH 128) of LDS rings and 512 threads -> one per CU;
+// VALU kernel: 64 threads, <= 33 KB LDS
+int attention_wgs_per_cu(int act, int dh) { return mfma_path(act, dh) ? 1 : 4; }
 
 hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s) {
   const int waves = a.R * (a.hq + 2 * a.hkv);
@@ -595,11 +620,13 @@ hipError_t launch_kv_append(const float* kself, const float* vself, int n, int h
 
 hipError_t launch_attention(const AttnArgs& a, int act, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  if (act == ACT_BF16 && a.dh == 128) {
-    hipLaunchKernelGGL(attn_mfma_kernel, dim3(n_work), dim3(512), 0, s, a);
-  } else if (act == ACT_BF16) {
-    if (a.dh != 64) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_valu_kernel<bf16, 64>), dim3(n_work), dim3(64), 0, s, a);
+  if (act == ACT_BF16) {
+    if (a.dh == 128)
+      hipLaunchKernelGGL(attn_mfma_kernel<128>, dim3(n_work), dim3(512), 0, s, a);
+    else if (a.dh == 64)
+      hipLaunchKernelGGL(attn_mfma_kernel<64>, dim3(n_work), dim3(512), 0, s, a);
+    else
+      return hipErrorInvalidValue;
   } else {
     if (a.dh == 64)
       hipLaunchKernelGGL((attn_valu_kernel<float, 64>), dim3(n_work), dim3(64), 0, s, a);

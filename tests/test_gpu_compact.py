@@ -6,13 +6,15 @@ leave the GEMMs, the attention and its partial results.
   live rows are every reachable row, in the host planner's order, and the attention splits are
   the host planner's, so the results are bit-identical to those of the solve that keeps the
   rows planned from reachability (KNAPSPEC_KEEP_PRUNED_ROWS) -- one and several sequences,
-  float32 and bfloat16, windows of 1, 2 and 3 tokens, with and without the LM-head estimate.
+  float32 and bfloat16 (head sizes 128 and 64), windows of 1, 2 and 3 tokens, with and
+  without the LM-head estimate.
 * Everything pruned after the first item (tau = 1.5): only the reference rows stay; results
   are bit-identical too (all budgets invalid).
 * Pruned for real (tau = 0.5, a skip cap): both plans pass parity against the oracle's DP
-  with the same pruning, one and several sequences (4 sequences x 200 budgets puts more than
-  512 rows in every item, so the MLP items get live-row plans too); the full Qwen3-1.7B preset
-  and the Llama-3-8B 32K preset at tau = 0.5 against the oracle's whole DP.
+  with the same pruning, one and several sequences, bfloat16 at head size 64 too (4 sequences
+  x 200 budgets puts more than 512 rows in every item, so the MLP items get live-row plans
+  too); the full Qwen3-1.7B preset and the Llama-3-8B 32K preset at tau = 0.5 against the
+  oracle's whole DP.
 """
 import math
 
@@ -67,6 +69,11 @@ def _bf16_gqa():
                   name="bf16_gqa_live")
 
 
+def _bf16_dh64():
+    return scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=3, d_model=512, n_q_heads=8,
+                  n_kv_heads=2, head_dim=64, d_ff=1024, name="bf16_dh64_live")
+
+
 def test_nothing_pruned_tiny_f32():
     res = _bit_equal(WORKLOADS["tiny"], None, tau=-2.0)
     assert res.valid.sum() > 1
@@ -74,6 +81,10 @@ def test_nothing_pruned_tiny_f32():
 
 def test_nothing_pruned_bf16_three_sequences():
     _bit_equal(_bf16_gqa(), [333, 1000, 77], tau=-2.0, n_budgets=48)
+
+
+def test_nothing_pruned_bf16_head_dim_64():
+    _bit_equal(_bf16_dh64(), [700, 90, 2000], tau=-2.0, n_budgets=64)
 
 
 def test_nothing_pruned_window3_skip_cap():
@@ -126,6 +137,11 @@ def test_pruned_parity_bf16_three_sequences():
     wl = _bf16_gqa()
     for flags in (3, 3 | KEEP):
         run_case(wl, ctxs=[333, 1000, 77], tau=0.5, n_budgets=48, flags=flags)
+
+
+def test_pruned_parity_bf16_head_dim_64():
+    for flags in (3, 3 | KEEP):
+        run_case(_bf16_dh64(), ctxs=[700, 90, 2000], tau=0.5, n_budgets=64, flags=flags)
 
 
 @pytest.mark.timeout(900)

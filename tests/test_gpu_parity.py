@@ -118,6 +118,15 @@ def test_bf16_head_dim_64():
     run_case(wl, ctxs=[200], n_budgets=40)
 
 
+def test_bf16_head_dim_64_query_blocks_and_splits():
+    # head size 64 on the MFMA kernel: a GQA group of 4 with up to 96 rows per item puts a KV
+    # head's query rows in two 256-row blocks; a context of 3000 (47 key tiles, the last one
+    # ragged) splits over several workgroups; 450 and an empty cache share the solve
+    wl = scaled(WORKLOADS["llama3_8b_32k"], n_layers=4, d_model=1024, n_q_heads=16,
+                n_kv_heads=4, head_dim=64, d_ff=2048, name="bf16_dh64_qblocks")
+    run_case(wl, ctxs=[3000, 450, 0], n_budgets=96)
+
+
 def test_bf16_multi_sequence():
     wl = scaled(WORKLOADS["llama3_8b_x16"], n_layers=3, d_model=512, n_q_heads=8,
                 n_kv_heads=2, d_ff=1024, n_seqs=3, ctx_range=None, name="multi_small")
