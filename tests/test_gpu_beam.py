@@ -99,6 +99,12 @@ def test_bf16_beam_mfma_path():
     run_beam(wl, 4, ctx=700, n_budgets=48)
 
 
+def test_bf16_beam_head_dim_64():
+    wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=3, d_model=512, n_q_heads=8,
+                n_kv_heads=2, head_dim=64, d_ff=1024, name="dh64_beam")
+    run_beam(wl, 4, ctx=700, n_budgets=48)
+
+
 def test_qwen3_1p7b_full_preset_beam4():
     # the full Qwen3-1.7B preset (28 layers, n = 4096, 128 budgets) keeping 4 states per cell
     run_beam(WORKLOADS["qwen3_1p7b_4k"], 4, ctx=4096)

@@ -84,6 +84,13 @@ def test_bf16_draft_verify():
     assert any(k > 0 for _, _, _, k in out)
 
 
+def test_bf16_draft_verify_head_dim_64():
+    wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=3, d_model=512, n_q_heads=8,
+                n_kv_heads=2, head_dim=64, d_ff=1024, name="dh64_draft")
+    out = run_draft(wl, 500, 5, 2048, _masks)
+    assert any(k > 0 for _, _, _, k in out)
+
+
 def test_repeated_calls_replay_the_captured_graph():
     # eager, capture, then replays of the same configuration: identical tokens every time
     from workloads.device import DeviceProblem

@@ -100,6 +100,13 @@ def test_bf16_window_mfma_path():
     run_window(wl, 4, ctx=1000, n_budgets=64)
 
 
+def test_bf16_window_head_dim_64():
+    # head size 64 on the MFMA kernel with r = 4 window rows per state
+    wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=3, d_model=512, n_q_heads=8,
+                n_kv_heads=2, head_dim=64, d_ff=1024, name="dh64_window")
+    run_window(wl, 4, ctx=900, n_budgets=48)
+
+
 def test_tiny_f32_window_lm_head_alpha():
     res, orc, rep = run_window(WORKLOADS["tiny"], 3, ctx=130, lm_vocab=512)
     # float32, no near-ties: the same masks, so the same alphas and the same pick
