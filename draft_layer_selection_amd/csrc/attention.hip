@@ -22,45 +22,57 @@ namespace ks {
 namespace {
 
 // ------------------------------------------------------------------------------------
-// q/k/v finalisation: one wave per (row, head), lane j owns the RoPE pair (j, j + dh/2).
+// q/k/v finalisation: one wave per (row, head), lane j owns the RoPE pair (j, j + dh/2)
+// (dh <= 128, so one pair per lane).
 // ------------------------------------------------------------------------------------
 template <class T>
 __global__ __launch_bounds__(256) void qkv_kernel(QkvArgs a) {
   const int heads = a.hq + 2 * a.hkv;
-  const int widx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform: the row's metadata come through scalar loads
+  const int widx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (widx >= a.R * heads) return;
-  const int lane = threadIdx.x & 63;
-  const int r = widx / heads, hd = widx % heads;
+  const int j = threadIdx.x & 63;
   const int half = a.dh / 2;
+  if (j >= half) return;
+  const int r = widx / heads, hd = widx % heads;
+  const size_t split_stride = (size_t)a.R * a.ldp;
+  const size_t base = (size_t)r * a.ldp + (size_t)hd * a.dh;
+  // every split's loads in flight before the first addition; the sum keeps the split order
+  float p0[GEMM_MAX_SPLITS], p1[GEMM_MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < GEMM_MAX_SPLITS; ++s)
+    if (s < a.splits) {
+      p0[s] = a.P[s * split_stride + base + j];
+      p1[s] = a.P[s * split_stride + base + j + half];
+    }
+  // the row's RoPE pair, loaded for v heads too so that its loads overlap the splits'
   const float* rope = a.rope + ((size_t)a.row_seq[r] * a.wmax + a.row_tok[r]) * a.dh;
-  for (int j = lane; j < half; j += 64) {
-    const size_t base = (size_t)r * a.ldp + (size_t)hd * a.dh;
-    float x0 = a.P[base + j];
-    float x1 = a.P[base + j + half];
-    for (int s = 1; s < a.splits; ++s) {
-      x0 += a.P[(size_t)s * a.R * a.ldp + base + j];
-      x1 += a.P[(size_t)s * a.R * a.ldp + base + j + half];
+  const float c = rope[j], sn = rope[half + j];
+  float x0 = p0[0], x1 = p1[0];
+#pragma unroll
+  for (int s = 1; s < GEMM_MAX_SPLITS; ++s)
+    if (s < a.splits) {
+      x0 += p0[s];
+      x1 += p1[s];
     }
-    if (hd < a.hq + a.hkv) {  // q and k are rotated, v is not
-      const float c = rope[j], sn = rope[half + j];
-      const float y0 = x0 * c - x1 * sn;
-      const float y1 = x1 * c + x0 * sn;
-      x0 = y0;
-      x1 = y1;
-    }
-    if (hd < a.hq) {
-      T* q = (T*)a.Q + ((size_t)r * a.hq + hd) * a.dh;
-      q[j] = from_f32<T>(x0);
-      q[j + half] = from_f32<T>(x1);
-    } else if (hd < a.hq + a.hkv) {
-      float* k = a.kself + ((size_t)r * a.hkv + (hd - a.hq)) * a.dh;
-      k[j] = x0;
-      k[j + half] = x1;
-    } else {
-      float* v = a.vself + ((size_t)r * a.hkv + (hd - a.hq - a.hkv)) * a.dh;
-      v[j] = x0;
-      v[j + half] = x1;
-    }
+  if (hd < a.hq + a.hkv) {  // q and k are rotated, v is not
+    const float y0 = x0 * c - x1 * sn;
+    const float y1 = x1 * c + x0 * sn;
+    x0 = y0;
+    x1 = y1;
+  }
+  if (hd < a.hq) {
+    T* q = (T*)a.Q + ((size_t)r * a.hq + hd) * a.dh;
+    q[j] = from_f32<T>(x0);
+    q[j + half] = from_f32<T>(x1);
+  } else if (hd < a.hq + a.hkv) {
+    float* k = a.kself + ((size_t)r * a.hkv + (hd - a.hq)) * a.dh;
+    k[j] = x0;
+    k[j + half] = x1;
+  } else {
+    float* v = a.vself + ((size_t)r * a.hkv + (hd - a.hq - a.hkv)) * a.dh;
+    v[j] = x0;
+    v[j + half] = x1;
   }
 }
 
@@ -595,6 +607,7 @@ int attention_qblock(int act, int dh) { return mfma_path(act, dh) ? QB : 64; }
 int attention_wgs_per_cu(int act, int dh) { return mfma_path(act, dh) ? 1 : 4; }
 
 hipError_t launch_qkv(const QkvArgs& a, int act, hipStream_t s) {
+  if (a.splits < 1 || a.splits > GEMM_MAX_SPLITS || a.dh > 128) return hipErrorInvalidValue;
   const int waves = a.R * (a.hq + 2 * a.hkv);
   const dim3 grid((waves + 3) / 4), block(256);
   if (act == ACT_F32)

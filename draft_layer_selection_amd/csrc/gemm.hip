@@ -522,7 +522,7 @@ GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_fl
     int s = 1;
     if (mode != GEMM_SWIGLU) {
       s = std::max(1, 512 / std::max(1, p.n_tiles * p.m_tiles));
-      s = std::min(std::min(s, 16), std::max(1, kiters / 4));
+      s = std::min(std::min(s, GEMM_MAX_SPLITS), std::max(1, kiters / 4));
       while (s > 1 && (size_t)s * R * N > cap_floats) --s;
     }
     finish(s);
@@ -538,7 +538,7 @@ GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_fl
     // only above 128 rows.  Fitted to cold-weight timings of the Llama-3-8B shapes (q|k|v, O
     // and down projections, R = 32 .. 245, GEMM plus split reduction): within 2% of the best
     // tile and split count per shape, against 5% for a fixed 256-workgroup target.
-    const int smax = std::max(1, std::min(16, K / std::max(1, 4 * R)));
+    const int smax = std::max(1, std::min(GEMM_MAX_SPLITS, K / std::max(1, 4 * R)));
     double best = -1;
     for (int ng : {2, 4}) {
       if (ng == 4 && (N % 256 != 0 || R <= 128)) continue;
@@ -580,7 +580,7 @@ GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_fl
     // direct-load fallback kernel (N not a multiple of 128 or K of 64)
     const int tiles = p.n_tiles * p.m_tiles;
     s = std::max(1, 512 / std::max(1, tiles));
-    s = std::min(std::min(s, 16), std::max(1, kiters / 4));
+    s = std::min(std::min(s, GEMM_MAX_SPLITS), std::max(1, kiters / 4));
     while (s > 1 && (size_t)s * R * N > cap_floats) --s;
   }
   finish(s);

@@ -19,6 +19,9 @@ enum GemmMode : int { GEMM_PARTIAL = 0, GEMM_SWIGLU = 1 };
 
 constexpr int WIN_MAX = 16;  // largest window r (tokens per DP state or verification block)
 constexpr int BEAM_MAX = 8;  // largest beam width (states kept per DP cell)
+// largest K-split count of a GEMM; the kernels that add the splits issue one load per split
+// before the first addition
+constexpr int GEMM_MAX_SPLITS = 16;
 
 struct GemmArgs {
   const void* A;  // [R][lda] activations (bf16 or f32, same as W)

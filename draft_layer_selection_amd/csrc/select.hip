@@ -29,9 +29,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   const int r = (int)(idx / d4), e4 = (int)(idx % d4);
   const size_t split_stride = (size_t)a.R * a.d;
   const size_t off = (size_t)r * a.d + 4 * e4;
-  f32x4 v = *(const f32x4*)(a.P + off);
-  for (int s = 1; s < a.splits; ++s) v += *(const f32x4*)(a.P + s * split_stride + off);
   const f32x4 res = *(const f32x4*)(a.state_old + (size_t)a.row_state[r] * a.d + 4 * e4);
+  // every split's load in flight before the first addition; the sum keeps the split order
+  f32x4 p[GEMM_MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < GEMM_MAX_SPLITS; ++s)
+    if (s < a.splits) p[s] = *(const f32x4*)(a.P + s * split_stride + off);
+  f32x4 v = p[0];
+#pragma unroll
+  for (int s = 1; s < GEMM_MAX_SPLITS; ++s)
+    if (s < a.splits) v += p[s];
   *(f32x4*)(a.E + off) = res + v;
 }
 
@@ -221,20 +228,37 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
   const int qb = q * a.Bm + b;
   const int erow = a.exec_row[(size_t)qb * a.kmax];
   const int src = b - inf.w;
-  const bool has_exec = erow >= 0 && src >= 0 && a.valid_old[(size_t)(q * a.Bm + src) * a.kmax];
-  const bool has_skip = a.valid_old[(size_t)qb * a.kmax] != 0;
-  const float* e_row = a.E + (size_t)(has_exec ? erow : 0) * a.d;
+  const float* e_row = a.E + (size_t)(erow >= 0 ? erow : 0) * a.d;
   const float* g_row = st_old + (size_t)b * slot;
-
-  f32x4 ev[IT], gv[IT];
-  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  // The validity flags and both candidates' mask words are requested first and the rows right
+  // after, without waiting in between (every address is in range); a row that takes no part
+  // is replaced by zeros below, as if it had not been read.
+  const int v_src = a.valid_old[(size_t)(q * a.Bm + (src >= 0 ? src : 0)) * a.kmax];
+  const int v_skip = a.valid_old[(size_t)qb * a.kmax];
+  uint64_t mask_exec = 0, mask_skip = 0;
+  if (threadIdx.x < a.mw) {
+    mask_exec = a.mask_old[((size_t)q * a.Bm + (src >= 0 ? src : 0)) * a.kmax * a.mw + threadIdx.x];
+    mask_skip = a.mask_old[(size_t)qb * a.kmax * a.mw + threadIdx.x];
+  }
+  f32x4 rv[IT], ev[IT], gv[IT];
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
     const int e4 = threadIdx.x + i * SELR_THREADS;
     const bool in = e4 < d4;
-    const f32x4 r = (in && (has_exec || has_skip)) ? *(const f32x4*)(ref + 4 * e4) : zero;
-    ev[i] = (in && has_exec) ? *(const f32x4*)(e_row + 4 * e4) : zero;
-    gv[i] = (in && has_skip) ? *(const f32x4*)(g_row + 4 * e4) : zero;
+    rv[i] = in ? *(const f32x4*)(ref + 4 * e4) : zero;
+    ev[i] = in ? *(const f32x4*)(e_row + 4 * e4) : zero;
+    gv[i] = in ? *(const f32x4*)(g_row + 4 * e4) : zero;
+  }
+  const bool has_exec = erow >= 0 && src >= 0 && v_src != 0;
+  const bool has_skip = v_skip != 0;
+  const int nrow = a.next_row[(size_t)qb * a.kmax];
+
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const f32x4 r = (has_exec || has_skip) ? rv[i] : zero;
+    if (!has_exec) ev[i] = zero;
+    if (!has_skip) gv[i] = zero;
     acc[0] += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
     acc[1] += ev[i][0] * r[0] + ev[i][1] * r[1] + ev[i][2] * r[2] + ev[i][3] * r[3];
     acc[2] += ev[i][0] * ev[i][0] + ev[i][1] * ev[i][1] + ev[i][2] * ev[i][2] + ev[i][3] * ev[i][3];
@@ -265,16 +289,15 @@ __global__ __launch_bounds__(SELR_THREADS) void select_reg_kernel(SelectArgs a) 
     uint64_t mval = 0;
     if (alive) {
       if (take) {
-        mval = a.mask_old[((size_t)q * a.Bm + src) * a.kmax * a.mw + wd];
+        mval = mask_exec;
         if (wd == a.item / 64) mval |= (uint64_t)1 << (a.item % 64);
       } else {
-        mval = a.mask_old[(size_t)qb * a.kmax * a.mw + wd];
+        mval = mask_skip;
       }
     }
     a.mask_new[(size_t)qb * a.kmax * a.mw + wd] = mval;
   }
 
-  const int nrow = a.next_row[(size_t)qb * a.kmax];
   const float ms = (take ? acc[2] : acc[4]) / (float)a.d;
   const float scale = alive ? 1.0f / sqrtf(ms + a.eps) : 0.f;
   float* out = st_new + (size_t)b * slot;
@@ -702,6 +725,7 @@ __global__ __launch_bounds__(SEL_THREADS) void embed_kernel(const T* w, const in
 }  // namespace
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  if (a.splits < 1 || a.splits > GEMM_MAX_SPLITS) return hipErrorInvalidValue;
   const size_t n = (size_t)a.R * (a.d / 4);
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
