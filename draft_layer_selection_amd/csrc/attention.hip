@@ -496,10 +496,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------
 // combine: one wave per (row, query head).  All maxima are in the log2 domain.
 // ------------------------------------------------------------------------------------
+constexpr int CMB_SPLITS = 32;  // splits whose partial rows are all requested at once
+
 template <class T, int DH, int WK>  // WK: largest window token count of the launch (1 or 8)
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int EPL = DH / 64;  // consecutive dh elements per lane
-  const int widx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform: the row's metadata come through scalar loads
+  const int widx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (widx >= a.R * a.hq) return;
   const int lane = threadIdx.x & 63;
   const int r = widx / a.hq, h = widx % a.hq;
@@ -508,31 +511,71 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const AttnSeq S = a.seqs[a.row_seq[r]];
   if (r - S.row_off >= S.M) return;  // a row past the live rows of a live-row plan
   const int e0 = lane * EPL;
-  const T* q = (const T*)a.Q + ((size_t)r * a.hq + h) * DH + e0;
+  const int rl = r - S.row_off;
+  const size_t slot0 = attn_slot(S, 0, rl, a.hq, h);
+  const size_t split_stride = (size_t)S.M * a.hq;
+  const int ns = S.nsplit;
+  // Loads in the order they are needed, all issued before the first wait: the query and the
+  // own keys, the splits' (max, denominator), the own values, then the splits' partial rows.
   // window keys: the own keys of the rows of window tokens 0..tw of this state (tw = 0: the
   // row's own key only)
   const int tw = WK == 1 ? 0 : a.row_tok[r];
+  const T* q = (const T*)a.Q + ((size_t)r * a.hq + h) * DH + e0;
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = to_f32(q[e]);
+  float kw[WK][EPL], vw[WK][EPL];
+#pragma unroll
+  for (int k = 0; k < WK; ++k)
+    if (k <= tw) {
+      const float* ks = a.kself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kw[k][e] = ks[e];
+    }
+  // lane sp < nsplit holds split sp's (max, denominator); weights 2^(m_sp - M)
+  const bool has = lane < ns;
+  float m_ld = -INFINITY, l_ld = 0.f;
+  if (ns > 0) {  // no splits (an empty cache): no partial slots either
+    const size_t lslot = slot0 + (size_t)min(lane, ns - 1) * split_stride;
+    m_ld = a.Mpart[lslot];
+    l_ld = a.Lpart[lslot];
+  }
+#pragma unroll
+  for (int k = 0; k < WK; ++k)
+    if (k <= tw) {
+      const float* vs = a.vself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vw[k][e] = vs[e];
+    }
+  // the partial rows of the first CMB_SPLITS splits: whole groups of 8, a group's missing
+  // splits reading the group's last one (zeroed when added)
+  const float* op = a.Opart + slot0 * DH + e0;
+  float v[CMB_SPLITS][EPL];
+#pragma unroll
+  for (int g = 0; g < CMB_SPLITS / 8; ++g) {
+    if (8 * g >= ns) break;
+#pragma unroll
+    for (int j = 8 * g; j < 8 * g + 8; ++j) {
+      const float* pj = op + (size_t)min(j, ns - 1) * split_stride * DH;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[j][e] = pj[e];
+    }
+  }
+
   float s_w[WK];
 #pragma unroll
   for (int k = 0; k < WK; ++k) {
     s_w[k] = -INFINITY;
     if (k <= tw) {
-      const float* ks = a.kself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d = fmaf(to_f32(q[e]), ks[e], d);
+      for (int e = 0; e < EPL; ++e) d = fmaf(qv[e], kw[k][e], d);
       s_w[k] = warp_sum(d) * a.scale_log2;
     }
   }
   const size_t qrow = (size_t)r * a.hq + h;
-  const int rl = r - S.row_off;
-  const size_t slot0 = attn_slot(S, 0, rl, a.hq, h);
-  const size_t split_stride = (size_t)S.M * a.hq;
-  const int ns = S.nsplit;
-  // lane sp < nsplit holds split sp's (max, denominator); weights 2^(m_sp - M)
-  const bool has = lane < ns;
-  const float ms = has ? a.Mpart[slot0 + lane * split_stride] : -INFINITY;
-  const float ls = has ? a.Lpart[slot0 + lane * split_stride] : 0.f;
+  const float ms = has ? m_ld : -INFINITY;
+  const float ls = has ? l_ld : 0.f;
   float mx = fmaxf(warp_max(ms), s_w[0]);
 #pragma unroll
   for (int k = 1; k < WK; ++k)
@@ -547,34 +590,40 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (k <= tw) den += w_w[k];
   const float inv = 1.0f / den;
   float num[EPL];
-  {
-    const float* vs = a.vself + ((size_t)(r - tw) * a.hkv + c) * DH + e0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) num[e] = w_w[0] * vs[e];
-  }
+  for (int e = 0; e < EPL; ++e) num[e] = w_w[0] * vw[0][e];
 #pragma unroll
   for (int k = 1; k < WK; ++k) {
     if (k <= tw) {
-      const float* vs = a.vself + ((size_t)(r - tw + k) * a.hkv + c) * DH + e0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) num[e] = fmaf(w_w[k], vs[e], num[e]);
+      for (int e = 0; e < EPL; ++e) num[e] = fmaf(w_w[k], vw[k][e], num[e]);
     }
   }
-  // splits in groups of 8 with the loads of a group issued together (fixed summation order)
-  const float* op = a.Opart + slot0 * DH + e0;
-  for (int sp0 = 0; sp0 < ns; sp0 += 8) {
-    float v[8][EPL];
+  // splits added in order, in groups of 8 (a group's missing splits add 0 * 0)
+#pragma unroll
+  for (int g = 0; g < CMB_SPLITS / 8; ++g) {
+    if (8 * g >= ns) break;
+#pragma unroll
+    for (int j = 8 * g; j < 8 * g + 8; ++j) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), j));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, j < ns ? v[j][e] : 0.f, num[e]);
+    }
+  }
+  // splits past CMB_SPLITS (at most 64, one per lane), 8 at a time
+  for (int sp0 = CMB_SPLITS; sp0 < ns; sp0 += 8) {
+    float u[8][EPL];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float* pj = op + (size_t)(sp0 + j) * split_stride * DH;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) v[j][e] = sp0 + j < ns ? pj[e] : 0.f;
+      for (int e = 0; e < EPL; ++e) u[j][e] = sp0 + j < ns ? pj[e] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), min(sp0 + j, 63)));
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, v[j][e], num[e]);
+      for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, u[j][e], num[e]);
     }
   }
   T* out = (T*)a.O + qrow * DH + e0;
