@@ -4,8 +4,9 @@
 // query rows of the block (grouped-query: the hq/hkv query heads of a KV head are rows too).
 //
 //   qkv_finalize : sum GEMM K-splits, rotate q and k at position ctx (rotate-half RoPE with a
-//                  host-computed float64 angle table), write q / own k / own v.
-//   attn (MFMA)  : bf16, dh = 128.  S^T = K Q^T and O^T += V^T P^T on
+//                  host-computed float64 angle table), write q (bf16: times log2(e)/sqrt(dh),
+//                  the MFMA kernel's score units) / own k / own v.
+//   attn (MFMA)  : bf16, dh = 128 or 64.  S^T = K Q^T and O^T += V^T P^T on
 //                  v_mfma_f32_32x32x16_bf16 so that each lane owns one query row's scores
 //                  (softmax statistics need one cross-half exchange per 64-key tile).
 //   attn (VALU)  : float32 (or any dh <= 128) reference-grade kernel, one query per lane.
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(256) void qkv_kernel(QkvArgs a) {
   }
   if (hd < a.hq) {
     T* q = (T*)a.Q + ((size_t)r * a.hq + hd) * a.dh;
-    q[j] = from_f32<T>(x0);
-    q[j + half] = from_f32<T>(x1);
+    q[j] = from_f32<T>(x0 * a.q_scale);
+    q[j + half] = from_f32<T>(x1 * a.q_scale);
   } else if (hd < a.hq + a.hkv) {
     float* k = a.kself + ((size_t)r * a.hkv + (hd - a.hq)) * a.dh;
     k[j] = x0;
@@ -168,9 +169,12 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 //     each 16-lane group element (i % 4) of the 8 bytes addressed by lane 4e + i/4 as its
 //     element e; lane (g, e, q) therefore addresses V[key 4*(g/2) + e][dh 16*(g%2) + 4q ..+3]
 //     of the MFMA step and receives V^T[dh][4 consecutive keys] exactly as the MFMA wants.
-//   * softmax in the log2 domain on the hardware v_exp_f32: p = 2^(s*c - m*c),
-//     c = log2(e)/sqrt(dh), with a lazily raised reference m (raised, and O and l rescaled,
-//     only when a score exceeds it by more than 2^8 in p); exact because l carries the same m.
+//   * softmax in the log2 domain on the hardware v_exp_f32: q is stored times
+//     c = log2(e)/sqrt(dh) (by the q/k/v finalisation), so a score q.k is already in the
+//     exponent's units, and the first score MFMA of a tile starts from -m instead of 0: the
+//     accumulators hold q.k - m and p = 2^(accumulator), with no per-score shift.  The
+//     reference m is raised lazily (and O, l and the tile's scores shifted) only when a score
+//     exceeds it by more than 8, i.e. p above 2^8; exact because l carries the same m.
 //   * Software pipeline: iteration t issues the score MFMAs of tile t+1 between the
 //     exponentials and P.V MFMAs of tile t, so one wave keeps the matrix core and the vector
 //     ALU busy at once.  K of tile t is read in iteration t-1 and V in iteration t; tile t is
@@ -254,7 +258,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int k0 = sp * S.chunk;
   const int k1 = min(S.ctx, k0 + S.chunk);
   const int ntiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
-  const float cs = a.scale_log2;
 
   // this lane's query row as the B operand of S^T = K Q^T: 8 K-steps of 16 dh
   const bf16* qp = (const bf16*)a.Q + ((size_t)row * a.hq + h) * DH + hi * 8;
@@ -312,8 +315,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = -INFINITY, lsum = 0.f;  // m: reference max of raw scores, shared by lanes l, l^32
-  const float thresh = RESCALE_LOG2 / cs;
+  // q arrives scaled by log2(e)/sqrt(dh), so q.k is in the exponent's units.  m: the
+  // reference (shared by lanes l, l^32), -inf until the first tile sets it; negm = -m in every
+  // entry is the C operand of the first score MFMA of a tile, so the accumulators come out as
+  // q.k - m and p = 2^(accumulator) with no per-score shift
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 negm;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
 
   // Loop-invariant LDS byte offsets within a slot.  K read for K-step ks of key l32 (+32 per
   // key block): chunk 2ks + hi in slot chunk ^ swz_k(key).  V^T read (transposing) of lane
@@ -358,7 +367,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
     }
   };
-  // scores of the K-steps of group g (KSTEPS/4 of them) for both 32-key blocks
+  // scores of the K-steps of group g (KSTEPS/4 of them) for both 32-key blocks; the first
+  // K-step starts from -m
   auto qk_steps = [&](const unsigned char* kst, int g, f32x16 (&sc)[2]) {
     constexpr int PER = KSTEPS / 4;
 #pragma unroll
@@ -366,16 +376,16 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *(const bf16x8*)(kst + koff[ks] + kb * 32 * ROWB);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? negm : sc[kb], 0, 0, 0);
       }
   };
-  // probabilities of group g with reference mc; lane holds keys 8*(r/4) + 4*hi + r%4 of the
-  // 32-key block g/2, r = 8*(g%2) .. +7; returns their sum (of the rounded values)
-  auto probs = [&](const f32x16 (&sc)[2], int g, float mc, bf16x8& pf) {
+  // probabilities of group g (scores already less the reference); lane holds keys
+  // 8*(r/4) + 4*hi + r%4 of the 32-key block g/2, r = 8*(g%2) .. +7; returns their sum (of the
+  // rounded values)
+  auto probs = [&](const f32x16 (&sc)[2], int g, bf16x8& pf) {
     float l = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      pf[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[g >> 1][8 * (g & 1) + e], cs, -mc));
+    for (int e = 0; e < 8; ++e) pf[e] = (bf16)__builtin_amdgcn_exp2f(sc[g >> 1][8 * (g & 1) + e]);
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       bf16x2 pp;
@@ -408,34 +418,41 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
           if (key >= k1) scur[kb][r] = -INFINITY;
         }
     }
-    float mt = scur[0][0];
+    float mt = scur[0][0];  // the tile's largest score less the reference
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, scur[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, scur[1][r]);
     mt = pair_max(mt);
-    if (__builtin_amdgcn_ballot_w64(mt > m + thresh) != 0) {  // some reference too low: raise
-      const float mn = mt > m + thresh ? mt : m;
-      const float corr = __builtin_amdgcn_exp2f((m - mn) * cs);
+    float delta = 0.f;  // raise of the reference (all lanes alike where it is zero)
+    if (it == 0) {      // the first tile sets the reference to its largest score
+      delta = mt;
+      m = mt;
+    } else if (__builtin_amdgcn_ballot_w64(mt > RESCALE_LOG2) != 0) {  // some p above 2^8
+      delta = mt > RESCALE_LOG2 ? mt : 0.f;
+      const float corr = __builtin_amdgcn_exp2f(-delta);
       lsum *= corr;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= corr;
-      m = mn;
+      m += delta;
     }
-    const float mc = m * cs;
+    if (__builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        negm[r] = -m;
+        scur[0][r] -= delta;
+        scur[1][r] -= delta;
+      }
+    }
     // K(it+1) is stale past the last tile; those scores are never used
     const unsigned char* kst = &kring[(J + 1) % NR][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) snext[kb][r] = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       qk_steps(kst, g, snext);
       bf16x8 pf;
-      lsum += probs(scur, g, mc, pf);
+      lsum += probs(scur, g, pf);
       pv_group(J, g, pf);
     }
   };
@@ -451,10 +468,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     load_tile(2);
     attn_wait_lgkm0();
     asm volatile("s_barrier" ::: "memory");  // tiles 0 and 1 in LDS
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
     if (wactive) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) qk_steps(&kring[0][0], g, sa);
@@ -488,7 +501,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     }
   }
   if (hi == 0) {
-    a.Mpart[slot] = m * cs;  // log2 domain, like the combine kernel expects
+    a.Mpart[slot] = m;  // log2 domain, like the combine kernel expects
     a.Lpart[slot] = lsum;
   }
 }

@@ -22,9 +22,13 @@
 //     bytes, so the planner widens the tile (NG=4) when R > 128;
 //   * K-slice partial sums are reduced through LDS in a fixed order (deterministic); K is split
 //     across workgroups only to fill the 256 CUs, and the consumer adds the splits.
+// bf16 K-split projections with 65 .. 256 rows (gemm_areg_kernel): activations straight from L2
+//   into MFMA operand registers, weights staged through two LDS buffers, one 256-row tile, so
+//   each weight byte is fetched once and the pipeline fill is short (see the kernel's notes).
 // bf16 fallback (gemm_bf16_kernel): direct-to-register loads, 64-column tiles, any N % 64 == 0.
 // f32 path: plain LDS-tiled FMA kernel (the small float32 decoder only).
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -422,6 +426,201 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
   }
 }
 
+// Activations in registers, weights through LDS (rows 65 .. 256 of one item).
+//
+// Why: in gemm_lds_kernel a stage holds weight and activation rows in one ring, and vector
+// loads complete in issue order, so both streams are in flight to the same depth; at 256
+// rows an activation stage is twice the 128-column weight stage and only a third of the
+// 160 KB ring carries weight bytes (or two 128-row m-tiles fetch each weight line twice).
+// Here the activations go straight from L2 into the MFMA operand registers, and LDS holds
+// two weight stages only:
+//   * workgroup = 8 waves, tile = 128 weight rows (output columns) x 256 activation rows;
+//     wave w owns rows 32w .. 32w+31 and all 128 columns (4 accumulator blocks), so every
+//     weight byte is fetched from HBM once per item and every activation row once per tile;
+//   * K permutation: in 16-wide step ks of a 64-K stage, lane half hi supplies K elements
+//     32hi + 8ks .. +7 for both operands (the MFMA sums over whichever K it is given, as
+//     long as both operands agree), so a lane's activations for a stage are 64 contiguous
+//     bytes: four 16-byte loads, D stages ahead of their use, in D+1 register sets;
+//   * weights: every wave loads 2 of the stage's 16 1 KB chunks into registers D stages
+//     ahead (D register sets) and stores them to the LDS stage buffer one stage before use;
+//     the stage buffers alternate, and the barrier opening stage t (after each wave's LDS
+//     stores have completed) both publishes stage t and frees the buffer stage t+1 goes to;
+//   * only ordinary vector loads are in flight, which complete in issue order, so the
+//     compiler's waits before each use are exact (LDS-DMA loads mixed with register loads
+//     make it drain the whole queue before every use of a loaded register);
+//   * the loop is unrolled so register sets and stage buffers are compile-time constants;
+//   * epilogue straight from the accumulators: SwiGLU pairs gate block cb with up block cb+2
+//     in the same lane; K-split partial sums are stored per split (XCD-local split order).
+// Rows past the live count (r_live) are skipped a wave at a time: such a wave only helps to
+// stage the weights.
+constexpr int AREG_ROWS = 256;  // activation rows per tile
+constexpr int AREG_COLS = 128;  // weight rows (output columns) per tile
+constexpr int AREG_MIN_ROWS = 64;     // at or below: gemm_lds_kernel (deeper weight ring)
+constexpr int AREG_DEFAULT_DEPTH = 3;  // measured: depth 4 no faster, 5 spills registers
+
+template <int A, int B>
+struct Lcm {
+  static constexpr int gcd(int x, int y) { return y == 0 ? x : gcd(y, x % y); }
+  static constexpr int value = A / gcd(A, B) * B;
+};
+
+// Weight stage buffer I of the register-activation kernel: one LDS object per buffer, so the
+// compiler's alias analysis tells the buffer being stored from the one being read.
+template <int I>
+__device__ __forceinline__ unsigned char* areg_slot() {
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[AREG_COLS * 128];
+  return buf;
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void gemm_areg_kernel(GemmArgs a) {
+  constexpr int NAB = D + 1;  // activation register sets
+  constexpr int NWB = D;      // weight register sets
+  constexpr int U = Lcm<Lcm<NAB, NWB>::value, 2>::value;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+  const int total = a.n_tiles * a.splits;
+  const int L = xcd_tile(blockIdx.x, a.per_xcd);
+  if (L >= total) return;
+  const int sp = L / a.n_tiles;  // consecutive tiles (one XCD) share a K split
+  const int nt = L % a.n_tiles;
+  const int rlim = a.r_live ? min(a.R, *a.r_live) : a.R;
+  if (rlim <= 0) return;  // uniform across the workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const bool active = wave * 32 < rlim;  // wave-uniform
+  const int k0 = sp * a.k_chunk;
+  const int k1 = min(a.K, k0 + a.k_chunk);
+  const int nit = (k1 - k0) / 64;
+  if (nit <= 0) return;  // the planner never makes an empty split
+  const int last = nit - 1;
+  const bf16* W = (const bf16*)a.W;
+  const bf16* Ap = (const bf16*)a.A;
+
+  // weight chunks of this wave: q = w and w + 8 (8 stage rows each); lane -> row
+  // 8q + lane/8, 16-byte slot lane%8 of the row <- its global chunk (lane%8) ^ ((row>>1)%8),
+  // which keeps the operand reads below conflict-free
+  const bf16* wsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * (wave + 8 * j) + (lane >> 3);
+    const int cglob = (lane & 7) ^ ((r >> 1) & 7);
+    const int half = AREG_COLS / 2;
+    const int wrow = a.mode == GEMM_SWIGLU
+                         ? (r < half ? nt * half + r : a.ff + nt * half + (r - half))
+                         : nt * AREG_COLS + r;
+    wsrc[j] = W + (size_t)wrow * a.K + k0 + 8 * cglob;
+  }
+  // activations of this lane's row: K elements 32hi .. 32hi+31 of each stage
+  int arow = wave * 32 + l32;
+  arow = arow < rlim ? arow : rlim - 1;
+  if (a.amap) arow = a.amap[arow];
+  const bf16* asrc = Ap + (size_t)arow * a.lda + k0 + 32 * hi;
+
+  bf16x8 av[NAB][4];
+  u32x4 wv[NWB][2];
+  auto load_a = [&](auto bc, int stage) {
+    constexpr int b = decltype(bc)::value;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) av[b][ks] = *(const bf16x8*)(asrc + stage * 64 + 8 * ks);
+  };
+  auto load_w = [&](auto bc, int stage) {
+    constexpr int b = decltype(bc)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wv[b][j] = *(const u32x4*)(wsrc[j] + stage * 64);
+  };
+  auto store_w = [&](auto bc, auto sc) {
+    constexpr int b = decltype(bc)::value, sl = decltype(sc)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *(u32x4*)(areg_slot<sl>() + (wave + 8 * j) * 1024 + lane * 16) = wv[b][j];
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  // operand read offset of K step ks: stage row 32cb + l32 (block cb adds 4 KB), chunk
+  // 4hi + ks; the swizzle (row >> 1) % 8 does not depend on cb
+  int woff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) woff[ks] = l32 * 128 + 16 * ((4 * hi + ks) ^ ((l32 >> 1) & 7));
+
+  // C = whether this wave computes (instantiated once per case: straight-line code between
+  // the barriers)
+  auto run = [&](auto cc) {
+    constexpr bool C = decltype(cc)::value;
+    // prologue: weights 0 .. D-1 and activations 0 .. D in flight, weights 0 stored
+    static_for<NWB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      load_w(ic, min(i, last));
+      if constexpr (C) load_a(ic, min(i, last));
+    });
+    if constexpr (C) load_a(std::integral_constant<int, D>{}, min(D, last));
+    store_w(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    load_w(std::integral_constant<int, 0>{}, min(NWB, last));
+
+    // stage t (j = t % U): wait for this wave's LDS stores, barrier (stage t published,
+    // stage t-1 read out), MFMAs of stage t, store weights t+1 and load weights t+1+D into
+    // their register set, load activations t+D+1 into the set stage t used
+    auto stage = [&](auto jc, int t) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int sl = j % 2, b = j % NAB, bw = (j + 1) % NWB;
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      if constexpr (C) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 wop[4];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            wop[cb] = *(const bf16x8*)(areg_slot<sl>() + cb * 4096 + woff[ks]);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[b][ks], wop[cb], acc[cb], 0, 0, 0);
+        }
+      }
+      store_w(std::integral_constant<int, bw>{}, std::integral_constant<int, (j + 1) % 2>{});
+      load_w(std::integral_constant<int, bw>{}, min(t + 1 + NWB, last));
+      if constexpr (C) load_a(std::integral_constant<int, b>{}, min(t + NAB, last));
+    };
+    int t0 = 0;
+    for (; t0 + U <= nit; t0 += U)
+      static_for<U>([&](auto jc) { stage(jc, t0 + decltype(jc)::value); });
+    static_for<U>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if (t0 + j < nit) stage(jc, t0 + j);
+    });
+    // loads past the last stage (clamped) may still be writing registers
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+  if (active)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+  if (!active) return;
+
+  // accumulator layout: block cb, register r -> row 32w + 8(r/4) + 4hi + r%4, column
+  // 32cb + l32 of the tile
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int grow = wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (grow >= a.R) continue;
+    if (a.mode == GEMM_PARTIAL) {
+      float* prow = a.P + ((size_t)sp * a.R + grow) * a.ldp + nt * AREG_COLS + l32;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) prow[32 * cb] = acc[cb][r];
+    } else {
+      bf16* hrow = (bf16*)a.H + (size_t)grow * a.ldh + nt * (AREG_COLS / 2) + l32;
+      hrow[0] = (bf16)(silu_f(acc[0][r]) * acc[2][r]);
+      hrow[32] = (bf16)(silu_f(acc[1][r]) * acc[3][r]);
+    }
+  }
+}
+
 // float32 path: tile 32 rows x 64 columns, K staged through LDS 32 at a time; thread
 // (ty, tx) owns rows {ty, ty+16} and columns tx*4..tx*4+3.
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
@@ -504,6 +703,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 }  // namespace
 
+// Activation stages in flight of the activations-in-registers GEMM (0 = not used); the
+// KNAPSPEC_GEMM_AREG environment variable (0, 3 or 4) overrides the default, read once.
+int areg_depth() {
+  static const int depth = [] {
+    const char* e = std::getenv("KNAPSPEC_GEMM_AREG");
+    if (!e || !*e) return AREG_DEFAULT_DEPTH;
+    const int v = std::atoi(e);
+    return (v == 3 || v == 4) ? v : 0;
+  }();
+  return depth;
+}
+
 GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_floats) {
   GemmPlan p{};
   const int ncols = mode == GEMM_SWIGLU ? 2 * ff : N;
@@ -529,6 +740,24 @@ GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_fl
     return p;
   }
   const bool k_ok = K % 64 == 0;
+  const int areg = areg_depth();
+  if (areg > 0 && mode == GEMM_PARTIAL && k_ok && R > AREG_MIN_ROWS && R <= AREG_ROWS &&
+      N % AREG_COLS == 0) {
+    // activations-in-registers kernel (K-split projections only: on the SwiGLU GEMM it
+    // measured no faster than gemm_lds_kernel): one m-tile; K splits fill the 256 CUs, each
+    // split at least 2*(areg+1) stages long so the pipeline fill stays small
+    p.areg = areg;
+    p.ng = 0;
+    p.mb = AREG_ROWS / 32;
+    p.m_tiles = 1;
+    p.n_tiles = N / AREG_COLS;
+    int s = std::max(1, 256 / p.n_tiles);
+    s = std::min(s, GEMM_MAX_SPLITS);
+    s = std::max(1, std::min(s, kiters / (2 * (areg + 1))));
+    while (s > 1 && (size_t)s * R * N > cap_floats) --s;
+    finish(s);
+    return p;
+  }
   if (mode == GEMM_PARTIAL && k_ok && N % 128 == 0) {
     // K-split LDS kernel: pick the tile (64*ng columns x 32*mb rows) and split count with the
     // least modelled time: rounds of 256 workgroups x bytes each workgroup stages through LDS
@@ -594,6 +823,13 @@ hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s) {
   const dim3 grid(b.per_xcd * 8);
   if (act == ACT_F32) {
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, b);
+  } else if (a.areg > 0) {
+    if (a.m_tiles != 1 || a.R > AREG_ROWS) return hipErrorInvalidValue;
+    switch (a.areg) {
+      case 3: hipLaunchKernelGGL((gemm_areg_kernel<3>), grid, dim3(512), 0, s, b); break;
+      case 4: hipLaunchKernelGGL((gemm_areg_kernel<4>), grid, dim3(512), 0, s, b); break;
+      default: return hipErrorInvalidValue;
+    }
   } else if (a.ng == 4) {
     switch (a.mb) {
       case 1: hipLaunchKernelGGL((gemm_lds_kernel<4, 1, 4>), grid, dim3(512), 0, s, b); break;

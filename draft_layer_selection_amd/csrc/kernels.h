@@ -43,15 +43,18 @@ struct GemmArgs {
   int ff;
   int per_xcd;    // ceil(total tiles / 8): XCD-aware tile order
   int ng;         // LDS kernel: 64-column groups per tile (2 or 4); 0 = direct-load kernel
+  int areg;       // > 0: activations-in-registers kernel with this many stages of activation
+                  // loads in flight (128-column tiles, one tile of up to 256 rows, m_tiles 1)
   const int* amap;    // nullable [R]: A row of output row r is A[amap[r]] (live-row plan)
   const int* r_live;  // nullable device count: m-tiles starting at or past it are skipped
 };
 
 // Tile/split plan of one GEMM launch (chosen on the host, see plan_gemm).
 struct GemmPlan {
-  int ng, mb, m_tiles, n_tiles, splits, k_chunk;
+  int ng, mb, m_tiles, n_tiles, splits, k_chunk, areg;
 };
 GemmPlan plan_gemm(int act, int R, int N, int K, int mode, int ff, size_t cap_floats);
+int areg_depth();
 
 // ---------------------------------------------------------------------------------------
 // Attention over the shared KV cache (split over context positions) + combine with self.
@@ -80,14 +83,15 @@ __host__ __device__ inline size_t attn_slot(const AttnSeq& s, int sp, int r_loca
 }
 
 struct AttnArgs {
-  const void* Q;       // [R][hq][dh] activations (position-rotated, unscaled)
+  const void* Q;       // [R][hq][dh] activations (position-rotated; bf16: times log2(e)/sqrt(dh))
   int hq, hkv, dh;
   const int4* work;    // per workgroup: (seq, kv head, q block, split); seq < 0: no work
   const AttnSeq* seqs; // [n_seqs]
   float* Opart;        // [slots][dh] unnormalised partial outputs
   float* Mpart;        // [slots] running max (log2 domain)
   float* Lpart;        // [slots] partial denominators
-  float scale_log2;    // log2(e) / sqrt(dh)
+  float scale_log2;    // factor from q.k to the log2 domain: log2(e) / sqrt(dh) for float32
+                       // (q unscaled); the bf16 MFMA kernel takes q pre-scaled and ignores it
 };
 
 struct CombineArgs {
@@ -103,7 +107,7 @@ struct CombineArgs {
   const AttnSeq* seqs;
   const int* row_seq;  // [R]
   int R, hq, hkv, dh;
-  float scale_log2;
+  float scale_log2;    // q.k to the log2 domain: log2(e)/sqrt(dh) for float32, 1 for bf16 (q pre-scaled)
   void* O;             // [R][hq*dh] activations
 };
 
@@ -115,7 +119,8 @@ struct QkvArgs {
   const int* row_seq;  // [R]
   const int* row_tok;  // [R] window token t of the row
   int wmax;
-  void* Q;             // [R][hq][dh] activations
+  void* Q;             // [R][hq][dh] activations: the rotated query times q_scale
+  float q_scale;       // log2(e)/sqrt(dh) for bf16 (scores come out in the exponent's units), 1 for f32
   float* kself;        // [R][hkv][dh]
   float* vself;
 };

@@ -1036,6 +1036,10 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     prof_end(m, pk, st);
   }
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  // bf16: the query is stored times log2(e)/sqrt(dh) (the MFMA attention works in the
+  // exponent's units); float32 keeps it unscaled and scales each score
+  const float q_scale = m->act == ks::ACT_BF16 ? scale_log2 : 1.f;
+  const float score_scale = m->act == ks::ACT_BF16 ? 1.f : scale_log2;
 
   auto gemm = [&](const void* A, int lda, int R, const void* W, int K, int N, int mode,
                   int* splits_out, int kclass, const int* amap = nullptr,
@@ -1051,12 +1055,14 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
     g.mode = mode;
     const ks::GemmPlan p = ks::plan_gemm(m->act, R, N, K, mode, d.d_ff, m->p_floats);
     g.ng = p.ng;
+    g.areg = p.areg;
     g.mb = p.mb;
     g.m_tiles = p.m_tiles;
     g.n_tiles = p.n_tiles;
     g.splits = p.splits;
     g.k_chunk = p.k_chunk;
-    g.r_live = p.m_tiles > 1 ? r_live : nullptr;  // one m-tile always holds a live row
+    // one m-tile always holds a live row; the register-activation kernel skips dead waves
+    g.r_live = (p.m_tiles > 1 || p.areg) ? r_live : nullptr;
     if (mode == ks::GEMM_SWIGLU) {
       g.H = m->h;
       g.ldh = d.d_ff;
@@ -1135,6 +1141,7 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       qa.row_tok = d_rowtok + (size_t)i * m->Rmax;
       qa.wmax = Wm;
       qa.Q = m->q;
+      qa.q_scale = q_scale;
       qa.kself = m->kself;
       qa.vself = m->vself;
       int pk = prof_begin(m, KNAPSPEC_K_QKV_ROPE, st);
@@ -1150,7 +1157,7 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       aa.Opart = m->Opart;
       aa.Mpart = m->Mpart;
       aa.Lpart = m->Lpart;
-      aa.scale_log2 = scale_log2;
+      aa.scale_log2 = score_scale;
       pk = prof_begin(m, KNAPSPEC_K_ATTENTION, st);
       HIPCHK(ks::launch_attention(aa, m->act, work_cnt[l], st));
       prof_end(m, pk, st);
@@ -1169,7 +1176,7 @@ int solve_impl(knapspec_model* m, const knapspec_solve_args* args, knapspec_resu
       ca.hq = hq;
       ca.hkv = hkv;
       ca.dh = dh;
-      ca.scale_log2 = scale_log2;
+      ca.scale_log2 = score_scale;
       ca.O = m->o;
       pk = prof_begin(m, KNAPSPEC_K_COMBINE, st);
       HIPCHK(ks::launch_combine(ca, m->act, st));
@@ -1560,6 +1567,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
     g.mode = mode;
     const ks::GemmPlan p = ks::plan_gemm(m->act, 1, N, K, mode, d.d_ff, m->p_floats);
     g.ng = p.ng;
+    g.areg = p.areg;
     g.mb = p.mb;
     g.m_tiles = p.m_tiles;
     g.n_tiles = p.n_tiles;
@@ -1621,6 +1629,10 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
     HIPCHK(ks::launch_init(ia, st));
   }
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  // bf16: the query is stored times log2(e)/sqrt(dh) (the MFMA attention works in the
+  // exponent's units); float32 keeps it unscaled and scales each score
+  const float q_scale = m->act == ks::ACT_BF16 ? scale_log2 : 1.f;
+  const float score_scale = m->act == ks::ACT_BF16 ? 1.f : scale_log2;
   const int slots = m->n_cus * ks::attention_wgs_per_cu(m->act, dh);
   std::vector<double> samples(reps);
   for (int ci = 0; ci < n_ctx; ++ci) {
@@ -1676,6 +1688,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
         qa.row_tok = (const int*)(dp + o_rowtok);
         qa.wmax = 1;
         qa.Q = m->q;
+        qa.q_scale = q_scale;
         qa.kself = m->kself;
         qa.vself = m->vself;
         HIPCHK(ks::launch_qkv(qa, m->act, st));
@@ -1689,7 +1702,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
         aa.Opart = m->Opart;
         aa.Mpart = m->Mpart;
         aa.Lpart = m->Lpart;
-        aa.scale_log2 = scale_log2;
+        aa.scale_log2 = score_scale;
         HIPCHK(ks::launch_attention(aa, m->act, nw, st));
         ks::CombineArgs ca{};
         ca.Q = m->q;
@@ -1706,7 +1719,7 @@ KS_API int knapspec_profile_items(knapspec_model* m, const knapspec_seq* seq,
         ca.hq = hq;
         ca.hkv = hkv;
         ca.dh = dh;
-        ca.scale_log2 = scale_log2;
+        ca.scale_log2 = score_scale;
         ca.O = m->o;
         HIPCHK(ks::launch_combine(ca, m->act, st));
         e = gemm1(m->o, m->qdim, W.w_o, m->qdim, D, ks::GEMM_PARTIAL, &splits);
@@ -1755,6 +1768,7 @@ int run_gemm(knapspec_model* m, hipStream_t st, const void* A, int lda, int R, c
   g.mode = mode;
   const ks::GemmPlan p = ks::plan_gemm(m->act, R, N, K, mode, m->desc.d_ff, m->p_floats);
   g.ng = p.ng;
+  g.areg = p.areg;
   g.mb = p.mb;
   g.m_tiles = p.m_tiles;
   g.n_tiles = p.n_tiles;
@@ -1924,6 +1938,10 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
     }
   hipEvent_t* ev = m->dv_ev;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  // bf16: the query is stored times log2(e)/sqrt(dh) (the MFMA attention works in the
+  // exponent's units); float32 keeps it unscaled and scales each score
+  const float q_scale = m->act == ks::ACT_BF16 ? scale_log2 : 1.f;
+  const float score_scale = m->act == ks::ACT_BF16 ? 1.f : scale_log2;
   const int32_t* d_rowseq = (const int32_t*)(dp + o_rowseq);
   const int32_t* d_rowstate = (const int32_t*)(dp + o_rowstate);
   const int32_t* d_rowtok = (const int32_t*)(dp + o_rowtok);
@@ -1952,6 +1970,7 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
       qa.row_tok = d_rowtok;
       qa.wmax = R == 1 ? 1 : n;
       qa.Q = m->q;
+      qa.q_scale = q_scale;
       qa.kself = m->kself;
       qa.vself = m->vself;
       HIPCHK(ks::launch_qkv(qa, m->act, st));
@@ -1969,7 +1988,7 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
       aa.Opart = m->Opart;
       aa.Mpart = m->Mpart;
       aa.Lpart = m->Lpart;
-      aa.scale_log2 = scale_log2;
+      aa.scale_log2 = score_scale;
       HIPCHK(ks::launch_attention(aa, m->act, nwork[k], st));
       ks::CombineArgs ca{};
       ca.Q = m->q;
@@ -1986,7 +2005,7 @@ KS_API int knapspec_draft_verify(knapspec_model* m, const knapspec_seq* seq,
       ca.hq = hq;
       ca.hkv = hkv;
       ca.dh = dh;
-      ca.scale_log2 = scale_log2;
+      ca.scale_log2 = score_scale;
       ca.O = m->o;
       HIPCHK(ks::launch_combine(ca, m->act, st));
       rc = run_gemm(m, st, m->o, m->qdim, R, W.w_o, m->qdim, D, ks::GEMM_PARTIAL, &splits);
