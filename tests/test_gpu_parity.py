@@ -19,7 +19,9 @@ BETA = {"f32": 1e-5, "bf16": 2e-3}
 
 
 def run_case(wl, seed=0, ctxs=None, tau=-math.inf, cap=-1, n_budgets=None, per_item=None,
-             flags=3):
+             flags=3, prepare=None):
+    """Solve on the GPU and compare with the oracle's DP (P1-P4).  ``prepare(prob)`` may edit
+    the inputs (host and device copies alike) before the solve."""
     from workloads.device import DeviceProblem
 
     print(f"\n[case] {wl.name} L={wl.shape.n_layers} d={wl.shape.d_model} "
@@ -28,6 +30,8 @@ def run_case(wl, seed=0, ctxs=None, tau=-math.inf, cap=-1, n_budgets=None, per_i
           f"flags={flags}", flush=True)
     prob = DeviceProblem(wl, seed, ctxs=ctxs, keep_host=True,
                          max_budgets=n_budgets or wl.n_budgets)
+    if prepare is not None:
+        prepare(prob)
     B = n_budgets or wl.n_budgets
     res = prob.solve(n_budgets=B, tau=tau, max_skip_weight=cap, flags=flags)
     beta = BETA[wl.shape.dtype]
@@ -102,6 +106,37 @@ def test_bf16_small_mfma_path():
     wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=4, d_model=1024, d_ff=2048,
                 name="qwen_like_small")
     run_case(wl, ctxs=[1000], n_budgets=64)
+
+
+def _keys_scaled_by_tile_pairs(low: float, high: float):
+    """Scale the cached keys of 64-key tile t by ``low`` for even t and ``high`` for odd t
+    (powers of two: exact in bf16), in the oracle's copy and on the device alike."""
+    def prepare(prob):
+        import torch
+
+        from workloads import synth
+        for q in range(len(prob.ctxs)):
+            for l, (kb, vb) in enumerate(prob.host_kv[q]):
+                pos = np.arange(kb.shape[1])
+                f = np.where((pos // 64) % 2 == 1, high, low).astype(np.float32)
+                nb = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(kb) * f[None, :, None])
+                prob.host_kv[q][l] = (nb, vb)
+                dev = torch.from_numpy(np.ascontiguousarray(nb)).view(torch.bfloat16)
+                prob.k_cache[q][l].copy_(dev.to("cuda"))
+        torch.cuda.synchronize()
+    return prepare
+
+
+def test_bf16_reference_raised_inside_splits():
+    # keys of even 64-key tiles scaled by 1/2, of odd tiles by 8: a context split that starts
+    # on an even tile sets its reference there, and its next tile scores ~16 above it in the
+    # exponent's units (the presets' N(0,1) caches stay within the allowed 8), so the attention
+    # raises the reference inside the split -- O, l and the tile's scores shifted, the C
+    # operand of the next tile's first score MFMA reset -- at head sizes 128 and 64
+    for dh, hq, hkv in ((128, 16, 8), (64, 16, 4)):
+        wl = scaled(WORKLOADS["qwen3_1p7b_4k"], n_layers=2, d_model=1024, n_q_heads=hq,
+                    n_kv_heads=hkv, head_dim=dh, d_ff=2048, name=f"bf16_raise_dh{dh}")
+        run_case(wl, ctxs=[6000], n_budgets=48, prepare=_keys_scaled_by_tile_pairs(0.5, 8.0))
 
 
 def test_bf16_several_query_blocks():
