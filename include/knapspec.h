@@ -188,7 +188,12 @@ typedef struct {
  * the grid instead uses, per budget, the fraction of the window's tokens whose greedy token
  * -- argmax over the LM head of the RMSNorm'd final state, float32 logits, ties to the lower
  * index -- equals the full model's (review, free parameters: the window is used "for DP and
- * acceptance estimation"; reading of Eq. 9). */
+ * acceptance estimation"; reading of Eq. 9).
+ * Environment: KNAPSPEC_GRAPHS=0 (read at every solve) launches every kernel eagerly instead
+ * of replaying a captured HIP graph; KNAPSPEC_GEMM_AREG (read once per process) selects the
+ * GEMM of the K-split projections with 65..256 rows: 3 (default) or 4 stages of activation
+ * loads in flight on the register-activation kernel, 0 the LDS-ring kernel (results differ
+ * only by the order in which K is summed). */
 int knapspec_solve(knapspec_model* model, const knapspec_solve_args* args,
                    knapspec_result* result);
 
