@@ -369,6 +369,23 @@ KS_API int knapspec_item_weights(const knapspec_latency_model* lat, int32_t n_la
   return item_weights(lat, n_layers, ctx_len, n_budgets, t, w);
 }
 
+KS_API int knapspec_gemm_plan(int32_t bf16, int32_t rows, int32_t n_cols, int32_t k,
+                              int32_t swiglu, int32_t d_ff, int64_t cap_floats, int32_t* plan) {
+  if (!plan) return fail(KNAPSPEC_EINVAL, "NULL pointer argument");
+  if (rows < 1 || n_cols < 1 || k < 1 || cap_floats < 1)
+    return fail(KNAPSPEC_EINVAL, "rows, n_cols, k and cap_floats must be >= 1");
+  if (swiglu && (d_ff < 1 || n_cols != 2 * d_ff))
+    return fail(KNAPSPEC_EINVAL, "the SwiGLU GEMM has n_cols = 2 * d_ff");
+  if (bf16 && (n_cols % 64 || k % 64))  // what the model and LM-head checks admit
+    return fail(KNAPSPEC_EUNSUPPORTED, "bf16 GEMMs need n_cols and k multiples of 64");
+  const ks::GemmPlan p = ks::plan_gemm(bf16 ? ks::ACT_BF16 : ks::ACT_F32, rows, n_cols, k,
+                                       swiglu ? ks::GEMM_SWIGLU : ks::GEMM_PARTIAL, d_ff,
+                                       (size_t)cap_floats);
+  const int32_t out[8] = {p.ng, p.mb, p.m_tiles, p.n_tiles, p.splits, p.k_chunk, p.areg, 0};
+  for (int i = 0; i < 8; ++i) plan[i] = out[i];
+  return KNAPSPEC_OK;
+}
+
 KS_API int knapspec_tpt_select(const float* alpha, const double* t_draft, const uint8_t* valid,
                                int32_t n_budgets, double t_target, int32_t gamma_min,
                                int32_t gamma_max, int32_t* best_budget, int32_t* best_gamma,

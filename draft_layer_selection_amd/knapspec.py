@@ -91,6 +91,8 @@ SIGNATURES = {
     "knapspec_item_weights": (C.c_int, [C.POINTER(knapspec_latency_model), C.c_int32, C.c_int32,
                                         C.c_int32, C.POINTER(C.c_double),
                                         C.POINTER(C.c_int32)]),
+    "knapspec_gemm_plan": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                     C.c_int32, C.c_int64, C.POINTER(C.c_int32)]),
     "knapspec_set_profiling": (C.c_int, [C.c_void_p, C.c_int32]),
     "knapspec_get_kernel_times": (C.c_int, [C.c_void_p, C.POINTER(C.c_double),
                                             C.POINTER(C.c_int64), C.c_int32]),
@@ -127,6 +129,7 @@ knapspec_solve = lib.knapspec_solve
 knapspec_solve_static = lib.knapspec_solve_static
 knapspec_tpt_select = lib.knapspec_tpt_select
 knapspec_item_weights = lib.knapspec_item_weights
+knapspec_gemm_plan = lib.knapspec_gemm_plan
 knapspec_set_profiling = lib.knapspec_set_profiling
 knapspec_get_kernel_times = lib.knapspec_get_kernel_times
 knapspec_mask_words = lib.knapspec_mask_words
@@ -184,6 +187,14 @@ def item_weights(n_layers, ctx, n_budgets, attn_base, attn_per_token, mlp, fixed
     _check(knapspec_item_weights(C.byref(lat), n_layers, ctx, n_budgets, _ptr(t, C.c_double),
                                  _ptr(w, C.c_int32)), "knapspec_item_weights")
     return t, w
+
+
+def gemm_plan(rows, n_cols, k, swiglu=False, d_ff=0, bf16=True, cap_floats=1 << 40):
+    """knapspec_gemm_plan -> dict(ng, mb, m_tiles, n_tiles, splits, k_chunk, areg)."""
+    out = (C.c_int32 * 8)()
+    _check(knapspec_gemm_plan(int(bool(bf16)), rows, n_cols, k, int(bool(swiglu)), d_ff,
+                              int(cap_floats), out), "knapspec_gemm_plan")
+    return dict(zip(("ng", "mb", "m_tiles", "n_tiles", "splits", "k_chunk", "areg"), out[:7]))
 
 
 def fit_latency(n, t):

@@ -252,6 +252,19 @@ int knapspec_tpt_select(const float* alpha, const double* t_draft, const uint8_t
                         int32_t gamma_max, int32_t* best_budget, int32_t* best_gamma,
                         double* best_tpt);
 
+/* Host-only: the launch plan knapspec_solve uses for one GEMM of an item -- `rows` rows,
+ * output columns n_cols (2 * d_ff for the SwiGLU gate|up GEMM, swiglu != 0), inner size k,
+ * room for cap_floats partial sums (the model's workspace holds max(16 * min(R, 256), R) x
+ * the widest N) -- for bf16 (bf16 != 0) or float32 weights.  plan[0..7]: 64-column groups per
+ * tile of the LDS-ring kernel (0: another kernel), 32-row blocks per tile, m-tiles, n-tiles, K
+ * splits, K per split, activation stages in flight of the register-activation kernel (0: not
+ * that kernel), 0.  The KNAPSPEC_GEMM_AREG environment variable (see knapspec_solve) applies.
+ * Returns KNAPSPEC_EINVAL on a NULL plan or sizes < 1, KNAPSPEC_EUNSUPPORTED for bf16 sizes
+ * that are not multiples of 64 (shapes knapspec_load_model and knapspec_set_lm_head refuse).
+ * Needs no GPU. */
+int knapspec_gemm_plan(int32_t bf16, int32_t rows, int32_t n_cols, int32_t k, int32_t swiglu,
+                       int32_t d_ff, int64_t cap_floats, int32_t* plan);
+
 /* Host-only: the latencies t_i and integer weights w_i one solve uses for a sequence at
  * context length ctx_len (t: 2L doubles, w: 2L int32; either may be NULL).  Needs no GPU. */
 int knapspec_item_weights(const knapspec_latency_model* lat, int32_t n_layers, int32_t ctx_len,
