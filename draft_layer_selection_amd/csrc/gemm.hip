@@ -449,8 +449,8 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GemmArgs a) {
 //     compiler's waits before each use are exact (LDS-DMA loads mixed with register loads
 //     make it drain the whole queue before every use of a loaded register);
 //   * the loop is unrolled so register sets and stage buffers are compile-time constants;
-//   * epilogue straight from the accumulators: SwiGLU pairs gate block cb with up block cb+2
-//     in the same lane; K-split partial sums are stored per split (XCD-local split order).
+//   * epilogue straight from the accumulators: the K-split partial sums of each split
+//     (XCD-local split order); the SwiGLU GEMM stays on gemm_lds_kernel (not faster here).
 // Rows past the live count (r_live) are skipped a wave at a time: such a wave only helps to
 // stage the weights.
 constexpr int AREG_ROWS = 256;  // activation rows per tile
@@ -506,11 +506,7 @@ __global__ __launch_bounds__(512) void gemm_areg_kernel(GemmArgs a) {
   for (int j = 0; j < 2; ++j) {
     const int r = 8 * (wave + 8 * j) + (lane >> 3);
     const int cglob = (lane & 7) ^ ((r >> 1) & 7);
-    const int half = AREG_COLS / 2;
-    const int wrow = a.mode == GEMM_SWIGLU
-                         ? (r < half ? nt * half + r : a.ff + nt * half + (r - half))
-                         : nt * AREG_COLS + r;
-    wsrc[j] = W + (size_t)wrow * a.K + k0 + 8 * cglob;
+    wsrc[j] = W + (size_t)(nt * AREG_COLS + r) * a.K + k0 + 8 * cglob;
   }
   // activations of this lane's row: K elements 32hi .. 32hi+31 of each stage
   int arow = wave * 32 + l32;
@@ -609,15 +605,9 @@ __global__ __launch_bounds__(512) void gemm_areg_kernel(GemmArgs a) {
   for (int r = 0; r < 16; ++r) {
     const int grow = wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
     if (grow >= a.R) continue;
-    if (a.mode == GEMM_PARTIAL) {
-      float* prow = a.P + ((size_t)sp * a.R + grow) * a.ldp + nt * AREG_COLS + l32;
+    float* prow = a.P + ((size_t)sp * a.R + grow) * a.ldp + nt * AREG_COLS + l32;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) prow[32 * cb] = acc[cb][r];
-    } else {
-      bf16* hrow = (bf16*)a.H + (size_t)grow * a.ldh + nt * (AREG_COLS / 2) + l32;
-      hrow[0] = (bf16)(silu_f(acc[0][r]) * acc[2][r]);
-      hrow[32] = (bf16)(silu_f(acc[1][r]) * acc[3][r]);
-    }
+    for (int cb = 0; cb < 4; ++cb) prow[32 * cb] = acc[cb][r];
   }
 }
 
@@ -824,7 +814,7 @@ hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s) {
   if (act == ACT_F32) {
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, b);
   } else if (a.areg > 0) {
-    if (a.m_tiles != 1 || a.R > AREG_ROWS) return hipErrorInvalidValue;
+    if (a.m_tiles != 1 || a.R > AREG_ROWS || a.mode != GEMM_PARTIAL) return hipErrorInvalidValue;
     switch (a.areg) {
       case 3: hipLaunchKernelGGL((gemm_areg_kernel<3>), grid, dim3(512), 0, s, b); break;
       case 4: hipLaunchKernelGGL((gemm_areg_kernel<4>), grid, dim3(512), 0, s, b); break;
